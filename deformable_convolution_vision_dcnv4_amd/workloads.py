@@ -1,0 +1,89 @@
+"""The five DCNv4 forward workloads, with their synthetic input recipes.
+
+Shapes come from the FlashInternImage-T stages (stage groups 4/8/16/32 in the
+classification config quoted by the usage-guide page pwwt.cn/news/2159231,
+section "实战部署指南"), a high-resolution dense-prediction map and the Stable
+Diffusion latent U-Net that jsqmd.com/news/933833 section 2 modifies.  All
+inputs are synthetic and seeded; no dataset or trained weight is involved.
+"""
+import math
+from dataclasses import dataclass, field
+
+
+def out_dim(n, K, stride, pad, dil):
+    span = n + 2 * pad - dil * (K - 1) - 1
+    return span // stride + 1 if span >= 0 else 0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    N: int
+    H: int
+    W: int
+    G: int
+    Cg: int
+    dtypes: tuple
+    x_dist: tuple = ("normal", 1.0)
+    offset_dist: tuple = ("normal", 1.0)
+    mask_dist: tuple = ("normal", 1.0)
+    K: int = 3
+    stride: int = 1
+    pad: int = 1
+    dil: int = 1
+    offset_scale: float = 1.0
+    remove_center: bool = False
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def C(self):
+        return self.G * self.Cg
+
+    @property
+    def P(self):
+        return self.K * self.K - (1 if self.remove_center else 0)
+
+    def out_hw(self):
+        return (out_dim(self.H, self.K, self.stride, self.pad, self.dil),
+                out_dim(self.W, self.K, self.stride, self.pad, self.dil))
+
+    def units(self):
+        Ho, Wo = self.out_hw()
+        return self.N * Ho * Wo * self.G
+
+    def samples(self):
+        return self.units() * self.P
+
+    def algorithmic_bytes(self, dtype):
+        """x read once + offsets + weights + out written once."""
+        s = 4 if dtype == "f32" else 2
+        Ho, Wo = self.out_hw()
+        x = self.N * self.H * self.W * self.C
+        o = self.N * Ho * Wo * self.C
+        return s * (x + o + self.units() * 3 * self.P)
+
+    def describe(self, dtype):
+        return (f"{self.name}: N={self.N} H={self.H} W={self.W} C={self.C} "
+                f"(G={self.G}, Cg={self.Cg}) K={self.K} s{self.stride} p{self.pad} "
+                f"d{self.dil} {dtype}")
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 16, 16, 4, 16, ("f32",),
+                     offset_dist=("normal", 2.0), mask_dist=("normal", 1.0),
+                     note="small correctness case"),
+    "fiit_stage1": Workload("fiit_stage1", 64, 56, 56, 4, 16, ("f32", "f16"),
+                            offset_dist=("normal", 1.5), mask_dist=("normal", 0.5),
+                            note="FlashInternImage-T stage-1 shape"),
+    "fiit_stage3": Workload("fiit_stage3", 64, 14, 14, 16, 16, ("f16",),
+                            offset_dist=("normal", 3.0), mask_dist=("normal", 0.5),
+                            note="FlashInternImage-T stage-3 shape, heavy border clipping"),
+    "hires": Workload("hires", 2, 256, 256, 8, 16, ("bf16",),
+                      offset_dist=("normal", 8.0), mask_dist=("uniform", -1.0, 1.0),
+                      note="high-resolution dense-prediction shape"),
+    "sd_latent": Workload("sd_latent", 8, 64, 64, 8, 40, ("bf16",),
+                          offset_dist=("normal", 2.0),
+                          mask_dist=("normal", 1.0 / math.sqrt(8.0)),
+                          note="diffusion U-Net latent shape, Cg=40"),
+}

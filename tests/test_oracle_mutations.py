@@ -1,0 +1,61 @@
+"""The pins bite: each plausible mistake, planted in a COPY of the oracle
+source on the CPU, must make the pin suite fail.  (The real oracle is never
+modified; the mutated copies live in a temporary directory.)"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "dcnv4_oracle.c")
+
+MUTATIONS = {
+    "trunc_not_floor": ("const float fx = floorf(px), fy = floorf(py);",
+                        "const float fx = truncf(px), fy = truncf(py);"),
+    "planes_swapped": ("const float dx = dxs[k], dy = dys[k], m = ms[k];",
+                       "const float dx = dys[k], dy = dxs[k], m = ms[k];"),
+    "corner_dropped": ("for (int b = 0; b < 2; ++b) {\n                        const int yy",
+                       "for (int b = 0; b < 1; ++b) {\n                        const int yy"),
+    "weights_swapped": ("{ { mhy * hx, mhy * lx }, { mly * hx, mly * lx } }",
+                        "{ { mhy * lx, mhy * hx }, { mly * hx, mly * lx } }"),
+    "pad_sign": ("(float)(wo * stride - pad + j * dil)", "(float)(wo * stride + pad + j * dil)"),
+    "column_major_points": ("(float)(wo * stride - pad + j * dil));\n                const float py = fmaf(dy, offset_scale, (float)(ho * stride - pad + i * dil))",
+                            "(float)(wo * stride - pad + i * dil));\n                const float py = fmaf(dy, offset_scale, (float)(ho * stride - pad + j * dil))"),
+    "lost_negative_band": ("if (!(px > -1.0f && px < (float)W", "if (!(px >= 0.0f && px < (float)W"),
+    "abs_weights": ("const float mhy = m * hy, mly = m * ly;", "const float mhy = fabsf(m) * hy, mly = fabsf(m) * ly;"),
+    "scale_ignored": ("const float px = fmaf(dx, offset_scale,", "const float px = fmaf(dx, 1.0f,"),
+    "dilation_ignored": ("(float)(ho * stride - pad + i * dil)", "(float)(ho * stride - pad + i)"),
+    "edge_clamp_not_zero": (
+        "if (yy >= 0 && yy < H && xx >= 0 && xx < W)\n"
+        "                            v = xf[(((int64_t)n * H + yy) * W + xx)",
+        "if (1)\n"
+        "                            v = xf[(((int64_t)n * H + (yy < 0 ? 0 : yy >= H ? H - 1 : yy)) * W"
+        " + (xx < 0 ? 0 : xx >= W ? W - 1 : xx))"),
+    "round_toward_zero": ("double q = nearbyint(ldexp(a, mbits - e));", "double q = floor(ldexp(a, mbits - e));"),
+    "f64_one_axis_weight": ("const double wgt = (1.0 - fabs(py - qy)) * (1.0 - fabs(px - qx));",
+                            "const double wgt = (1.0 - fabs(py - qy));"),
+    "f64_planes_swapped": ("const double dx = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + k];",
+                           "const double dx = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + s.P + k];"),
+    "f64_skips_center_always": ("if (s.remove_center && i == K / 2 && j == K / 2) continue;\n                const double dx",
+                                "if (i == K / 2 && j == K / 2) continue;\n                const double dx"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    before, after = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(before) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(before, after, 1)
+    csrc = tmp_path / "mut.c"
+    csrc.write_text(mutated)
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC",
+                    "-o", str(so), str(csrc), "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, DCNV4_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-W", "ignore::RuntimeWarning",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch '{name}':\n{r.stdout[-2000:]}"
