@@ -1,0 +1,234 @@
+"""Benchmark: DCNv4 forward GB/s, Gsamples/s and fraction of MI355X HBM peak.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload fiit_stage1] [--dtype f16]
+
+One step = one launch of the whole operator (sampling, bilinear interpolation
+and weighted aggregation fused in one kernel) over one batch of the workload.
+Inputs are seeded and synthetic and already resident in HBM.  To keep each
+launch reading HBM rather than the 256 MB Infinity Cache, the timed loop
+rotates over several copies of the inputs (at least 1 GiB in all), so a copy
+is reused only after >= 1 GiB of other traffic.
+
+Printed: one JSON line (rank 0).  `value` = algorithmic bytes per step /
+wall-clock time per step over the timed region; `roofline.achieved` = the
+same bytes / the kernel's mean duration from per-launch HIP events on the
+launch stream.  Algorithmic bytes per (pixel, group) unit = (2*Cg + 3*P)*s:
+x read once, out written once, 2P offsets and P weights read once.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "deformable_convolution_vision_dcnv4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, dtype, launches_bytes):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{workload}_{dtype}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, dtype, x, off, m, budget_s):
+    """The CPU oracle (single-threaded C, as it stands) on the same inputs."""
+    from oracle import ref
+    kw = dict(K=wl.K, stride=wl.stride, pad=wl.pad, dil=wl.dil, offset_scale=wl.offset_scale,
+              remove_center=wl.remove_center)
+    # bounded sample: the first n images, sized to about budget_s of CPU work
+    n = 1
+    t0 = time.perf_counter()
+    ref.forward_f32(x[:n], off[:n], m[:n], dtype=dtype, **kw)
+    per_img = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(wl.N, budget_s / per_img)))
+    t0 = time.perf_counter()
+    ref.forward_f32(x[:n], off[:n], m[:n], dtype=dtype, **kw)
+    dt = time.perf_counter() - t0
+    bytes_ = wl.algorithmic_bytes(dtype) * n / wl.N
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {wl.N} images of the same workload, binary32-sequence oracle "
+                      f"(plain C, one thread), {dt:.1f} s",
+            "gsamples_per_s": round(wl.samples() * n / wl.N / dt / 1e9, 6)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="fiit_stage1")
+    ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's last)")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotating input copies")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the operator is measured on one GPU's share "
+              "(multi-GPU sharding is not part of this build); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from deformable_convolution_vision_dcnv4_amd import binding
+    from deformable_convolution_vision_dcnv4_amd import inputs as gen
+    from deformable_convolution_vision_dcnv4_amd.workloads import WORKLOADS
+
+    def log(*a):
+        if not args.quiet:
+            print("[bench]", *a, file=sys.stderr, flush=True)
+
+    wl = WORKLOADS[args.workload]
+    dtype = args.dtype or wl.dtypes[-1]
+    assert dtype in ("f32", "f16", "bf16")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    dcode = {"f32": binding.F32, "f16": binding.F16, "bf16": binding.BF16}[dtype]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+
+    log(f"workload {wl.describe(dtype)}; generating inputs (seed {wl.seed})")
+    x, off, m = gen.make_inputs(wl, dtype)
+
+    def to_dev(a):
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    Ho, Wo = wl.out_hw()
+    set_bytes = (x.nbytes + off.nbytes + m.nbytes + wl.N * Ho * Wo * wl.C * x.itemsize)
+    copies = int(min(64, max(2, -(-args.rotate_bytes * (1 << 30) // set_bytes))))
+    xs0, os0, ms0 = to_dev(x), to_dev(off), to_dev(m)
+    sets = []
+    for i in range(copies):
+        xi, oi, mi = (xs0, os0, ms0) if i == 0 else (xs0.clone(), os0.clone(), ms0.clone())
+        outi = torch.empty((wl.N, Ho, Wo, wl.C), dtype=tdt, device=dev)
+        sets.append((xi, oi, mi, outi))
+    torch.cuda.synchronize()
+    log(f"{copies} rotating input copies, {copies * set_bytes / 2**30:.2f} GiB")
+
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    L = binding.lib()
+    argv = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr(), wl.N, wl.H, wl.W,
+             wl.G, wl.Cg, wl.K, wl.stride, wl.pad, wl.dil, wl.offset_scale, dcode, sptr) for s in sets]
+    fwd = L.dcnv4_forward
+
+    def step(i):
+        st = fwd(*argv[i % copies])
+        if st != 0:
+            raise RuntimeError(f"dcnv4_forward failed: {binding.status_string(st)}: {binding.last_error()}")
+
+    plan = binding.query_plan(sets[0][0], sets[0][1], sets[0][2], sets[0][3], kernel_size=wl.K,
+                              stride=wl.stride, pad=wl.pad, dilation=wl.dil, offset_scale=wl.offset_scale)
+    log(f"plan {plan}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    # timed region: K back-to-back launches
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = ev0.elapsed_time(ev1)
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, events {region_ms:.3f} ms")
+
+    # per-launch HIP events on the launch stream: the kernel's own duration
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+    kern_ms = float(np.mean(durs))
+    log(f"per-launch events: mean {kern_ms * 1e3:.2f} us, median {np.median(durs) * 1e3:.2f} us, "
+        f"p10 {np.percentile(durs, 10) * 1e3:.2f} us, p90 {np.percentile(durs, 90) * 1e3:.2f} us")
+
+    alg_bytes = wl.algorithmic_bytes(dtype)
+    ms_per_step = wall * 1e3 / args.steps
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = load_traffic(wl.name, dtype, alg_bytes)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        cpu = cpu_baseline(wl, dtype, x, off, m, args.cpu_budget)
+
+    rec = {
+        "metric": "DCNv4 fwd GB/s + Gsamples/s per MI355X; % of HBM roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded counter-based generator; no dataset, no trained weights)",
+        "config": {
+            "workload": wl.describe(dtype),
+            "N": wl.N, "H": wl.H, "W": wl.W, "G": wl.G, "Cg": wl.Cg, "K": wl.K,
+            "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil, "offset_scale": wl.offset_scale,
+            "inputs": {"x": list(wl.x_dist), "offset": list(wl.offset_dist), "mask": list(wl.mask_dist),
+                       "seed": wl.seed},
+            "algorithmic_bytes_per_step": alg_bytes,
+            "samples_per_step": wl.samples(),
+            "rotating_copies": copies,
+            "plan": plan,
+        },
+        "gsamples_per_s": round(wl.samples() / (ms_per_step * 1e-3) / 1e9, 3),
+        "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "kernel_us_mean": round(kern_ms * 1e3, 3),
+        "kernel_us_median": round(float(np.median(durs)) * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,47 @@
+"""Build libdcnv4.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m deformable_convolution_vision_dcnv4_amd.build [--asm DIR]
+
+Flags: contraction off (the binary32 operation order is part of the
+operator's contract), packed-fp32 instructions disabled, -O3.
+"""
+import argparse
+import glob
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdcnv4.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+             "-ffp-contract=off", "-fno-gpu-rdc",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose=False, asm_dir=None):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    cmd = [hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-shared", "-o", LIB + ".tmp"] + sources()
+    if asm_dir:
+        os.makedirs(asm_dir, exist_ok=True)
+        cmd += ["-save-temps=obj"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=asm_dir or CSRC)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", default=None, help="keep intermediate files (ISA) in this directory")
+    args = ap.parse_args()
+    print(build(verbose=True, asm_dir=args.asm))

@@ -1,0 +1,240 @@
+// DCNv4 forward: the C ABI (include/dcnv4.h) -- validation, planning, launch.
+//
+// Every argument is checked on the host before the first HIP call, so an
+// invalid call launches nothing and writes nothing.  The only global state is
+// a per-device cache of "is this a gfx950 device", filled on first use.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "dcnv4.h"
+#include "dcnv4_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int out_dim(int in, int K, int stride, int pad, int dil)
+{
+    if (in < 1 || K < 1 || stride < 1 || pad < 0 || dil < 1) return 0;
+    const int64_t span = (int64_t)in + 2 * (int64_t)pad - (int64_t)dil * (K - 1) - 1;
+    if (span < 0) return 0;
+    const int64_t o = span / stride + 1;
+    return o > INT32_MAX ? 0 : (int)o;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Validate and fill a Problem.  Returns DCNV4_OK or an error status.
+int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* mask,
+             const void* out, int N, int H, int W, int G, int Cg, int K, int stride,
+             int pad, int dil, float offset_scale, int remove_center,
+             int64_t offset_row, int64_t mask_row, int dtype)
+{
+    g_last_error[0] = '\0';
+    if (dtype != DCNV4_F32 && dtype != DCNV4_F16 && dtype != DCNV4_BF16)
+        return fail(DCNV4_ERR_DTYPE, "dtype %d is not f32 (0), f16 (1) or bf16 (2)", dtype);
+    if (N < 0 || H < 1 || W < 1 || G < 1 || Cg < 1)
+        return fail(DCNV4_ERR_SHAPE, "need N >= 0 and H, W, G, Cg >= 1 (got N=%d H=%d W=%d G=%d Cg=%d)",
+                    N, H, W, G, Cg);
+    if (K < 1 || stride < 1 || dil < 1 || pad < 0)
+        return fail(DCNV4_ERR_PARAM, "need K, stride, dilation >= 1 and pad >= 0 (got K=%d s=%d d=%d p=%d)",
+                    K, stride, dil, pad);
+    if (!isfinite(offset_scale))
+        return fail(DCNV4_ERR_PARAM, "offset_scale is not finite");
+    if (remove_center != 0 && remove_center != 1)
+        return fail(DCNV4_ERR_PARAM, "remove_center must be 0 or 1");
+    if (remove_center && (K % 2 == 0 || K < 3))
+        return fail(DCNV4_ERR_PARAM, "remove_center needs an odd K >= 3 (got K=%d)", K);
+    if (H >= (1 << 24) || W >= (1 << 24))
+        return fail(DCNV4_ERR_TOO_LARGE, "H and W must be < 2^24 (positions are exact in binary32)");
+    if ((int64_t)K * K > 1024)
+        return fail(DCNV4_ERR_PARAM, "K*K must be <= 1024");
+    const int Ho = out_dim(H, K, stride, pad, dil), Wo = out_dim(W, K, stride, pad, dil);
+    if (Ho < 1 || Wo < 1)
+        return fail(DCNV4_ERR_PARAM, "no output: Ho=%d Wo=%d", Ho, Wo);
+    const int P = K * K - remove_center;
+    const int64_t C = (int64_t)G * Cg;
+    if (C >= ((int64_t)1 << 31))
+        return fail(DCNV4_ERR_TOO_LARGE, "G*Cg must be < 2^31");
+    const int64_t dense_off = (int64_t)G * 2 * P, dense_mask = (int64_t)G * P;
+    if (offset_row == 0) offset_row = dense_off;
+    if (mask_row == 0) mask_row = dense_mask;
+    if (offset_row < dense_off || mask_row < dense_mask)
+        return fail(DCNV4_ERR_PARAM, "row strides must be >= G*2*P (%lld) and G*P (%lld)",
+                    (long long)dense_off, (long long)dense_mask);
+    if ((int64_t)H * W * C >= ((int64_t)1 << 31) || (int64_t)Ho * Wo * C >= ((int64_t)1 << 31))
+        return fail(DCNV4_ERR_TOO_LARGE, "one image of x or out must hold < 2^31 elements");
+    const int64_t units = (int64_t)N * Ho * Wo * G;
+    if (units >= ((int64_t)1 << 31))
+        return fail(DCNV4_ERR_TOO_LARGE, "N*Ho*Wo*G must be < 2^31");
+
+    p->x = x; p->off = offset; p->msk = mask; p->out = (void*)out;
+    p->N = N; p->H = H; p->W = W; p->G = G; p->Cg = Cg; p->K = K; p->P = P;
+    p->stride = stride; p->pad = pad; p->dil = dil; p->Ho = Ho; p->Wo = Wo;
+    p->remove_center = remove_center; p->off_row = offset_row; p->mask_row = mask_row;
+    p->offset_scale = offset_scale; p->dtype = dtype;
+    if (N == 0) return DCNV4_OK;
+
+    if (!x || !offset || !mask || !out)
+        return fail(DCNV4_ERR_NULL, "null pointer (x=%p offset=%p mask=%p out=%p)", x, offset, mask, out);
+    const int s = dtype == DCNV4_F32 ? 4 : 2;
+    if ((uintptr_t)x % s || (uintptr_t)offset % s || (uintptr_t)mask % s || (uintptr_t)out % s)
+        return fail(DCNV4_ERR_ALIGN, "pointers must be aligned to the %d-byte element size", s);
+    const int64_t npix_out = (int64_t)N * Ho * Wo;
+    const int64_t xbytes = (int64_t)N * H * W * C * s;
+    const int64_t obytes = npix_out * C * s;
+    const int64_t offbytes = ((npix_out - 1) * offset_row + dense_off) * s;
+    const int64_t mbytes = ((npix_out - 1) * mask_row + dense_mask) * s;
+    if (overlaps(out, obytes, x, xbytes) || overlaps(out, obytes, offset, offbytes) ||
+        overlaps(out, obytes, mask, mbytes))
+        return fail(DCNV4_ERR_ALIAS, "out overlaps an input");
+    return DCNV4_OK;
+}
+
+// Is the current device a gfx950?  Cached per device id.
+int check_device()
+{
+    static std::mutex mu;
+    static int cache[64];   // 0 unknown, 1 yes, 2 no
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(DCNV4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64)
+        return fail(DCNV4_ERR_HIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(DCNV4_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (cache[dev] == 2)
+            return fail(DCNV4_ERR_HIP, "device %d is %s; this library is built for gfx950", dev,
+                        prop.gcnArchName);
+    }
+    if (cache[dev] != 1)
+        return fail(DCNV4_ERR_HIP, "device %d is not a gfx950", dev);
+    return DCNV4_OK;
+}
+
+int forward_impl(const void* x, const void* offset, const void* mask, void* out,
+                 int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,
+                 float offset_scale, int remove_center, int64_t offset_row, int64_t mask_row,
+                 int dtype, void* stream)
+{
+    dcnv4::Problem p;
+    int st = validate(&p, x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dil,
+                      offset_scale, remove_center, offset_row, mask_row, dtype);
+    if (st != DCNV4_OK || N == 0) return st;
+    st = check_device();
+    if (st != DCNV4_OK) return st;
+    dcnv4::Plan plan;
+    dcnv4::make_plan(p, &plan);
+    const hipError_t e = dcnv4::launch_forward(p, plan, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(DCNV4_ERR_HIP, "launch of %s failed: %s", dcnv4_kernel_name(plan.kernel),
+                    hipGetErrorString(e));
+    return DCNV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dcnv4_forward(const void* x, const void* offset, const void* mask, void* out,
+                  int N, int H, int W, int G, int Cg,
+                  int K, int stride, int pad, int dilation, float offset_scale,
+                  int dtype, void* stream)
+{
+    return forward_impl(x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dilation,
+                        offset_scale, 0, 0, 0, dtype, stream);
+}
+
+int dcnv4_forward_ex(const void* x, const void* offset, const void* mask, void* out,
+                     int N, int H, int W, int G, int Cg,
+                     int K, int stride, int pad, int dilation, float offset_scale,
+                     int remove_center, int64_t offset_row, int64_t mask_row,
+                     int dtype, void* stream)
+{
+    return forward_impl(x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dilation,
+                        offset_scale, remove_center, offset_row, mask_row, dtype, stream);
+}
+
+int dcnv4_output_dim(int in, int K, int stride, int pad, int dilation)
+{
+    return out_dim(in, K, stride, pad, dilation);
+}
+
+const char* dcnv4_status_string(int status)
+{
+    switch (status) {
+        case DCNV4_OK: return "ok";
+        case DCNV4_ERR_NULL: return "null pointer";
+        case DCNV4_ERR_SHAPE: return "invalid shape";
+        case DCNV4_ERR_PARAM: return "invalid parameter";
+        case DCNV4_ERR_DTYPE: return "invalid dtype";
+        case DCNV4_ERR_ALIAS: return "output overlaps an input";
+        case DCNV4_ERR_TOO_LARGE: return "problem too large";
+        case DCNV4_ERR_HIP: return "HIP error";
+        case DCNV4_ERR_ALIGN: return "misaligned pointer";
+        default: return "unknown status";
+    }
+}
+
+const char* dcnv4_last_error(void) { return g_last_error; }
+
+const char* dcnv4_version(void) { return "0.1.0"; }
+
+int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const void* out,
+                     int N, int H, int W, int G, int Cg,
+                     int K, int stride, int pad, int dilation, float offset_scale,
+                     int remove_center, int64_t offset_row, int64_t mask_row,
+                     int dtype, dcnv4_plan* plan)
+{
+    if (!plan) return fail(DCNV4_ERR_NULL, "plan is null");
+    dcnv4::Problem p;
+    const int st = validate(&p, x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dilation,
+                            offset_scale, remove_center, offset_row, mask_row, dtype);
+    if (st != DCNV4_OK) return st;
+    dcnv4::Plan pl;
+    dcnv4::make_plan(p, &pl);
+    plan->vec = pl.vec;
+    plan->lanes_per_unit = pl.lanes;
+    plan->block = pl.block;
+    plan->grid = N == 0 ? 0 : pl.grid;
+    plan->kernel = pl.kernel;
+    return DCNV4_OK;
+}
+
+const char* dcnv4_kernel_name(int kernel)
+{
+    switch (kernel) {
+        case dcnv4::kKernelGatherVec: return "gather_vec";
+        default: return "none";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+/*
+ * dcnv4.h -- C ABI of libdcnv4.so: the DCNv4 spatial-aggregation forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (web pages on DCNv4):
+ *   "不只是卷积的平替：我把DCNv4塞进Stable Diffusion的U-Net里" (jsqmd.com/news/933833),
+ *   section 1, code example "DCNv4核心计算流程示例（简化版）": for every output
+ *   pixel and group, K*K sampling points sit on the regular convolution grid
+ *   moved by learned offsets; the input is bilinearly sampled at each point,
+ *   each sample is multiplied by its dynamic weight, and the weighted samples
+ *   are summed over the points.  Groups share nothing: output channel
+ *   g*Cg + c depends only on input channel g*Cg + c.
+ *   Same page, section 1, first optimisation, and "DCNv4：重塑视觉模型核心，三倍速率
+ *   的动态稀疏卷积如何炼成？" (bqwf.cn/news/1148139), section 2.1: the dynamic
+ *   weights are raw -- no softmax over the points; they may be negative and
+ *   may exceed 1.
+ *   "掌握DCNv4技术：3倍速度提升与80%加速效果的实战指南" (pwwt.cn/news/2159231),
+ *   section "进阶优化建议": offset_scale scales the offsets; an option drops the
+ *   centre point.
+ *
+ * Conventions fixed where the pages are silent:
+ *   - channels-last tensors; offsets and weights belong to OUTPUT pixels;
+ *   - offset row of one group = (2, P): plane 0 moves the point along W (x),
+ *     plane 1 along H (y); P = K*K points enumerated row-major, k = i*K + j,
+ *     i the row index (P = K*K - 1 with the centre removed, order otherwise
+ *     unchanged);
+ *   - point k of output pixel (ho, wo):
+ *       px = wo*stride - pad + j*dilation + offset_scale * dx[k]
+ *       py = ho*stride - pad + i*dilation + offset_scale * dy[k]
+ *   - bilinear sampling between floor(p) and floor(p)+1 per axis; pixels
+ *     outside the image read as zero; a point with px <= -1, px >= W,
+ *     py <= -1 or py >= H (or a NaN coordinate) contributes nothing;
+ *   - Ho = (H + 2*pad - dilation*(K-1) - 1) / stride + 1, the same for Wo.
+ *
+ * Arithmetic: every I/O type is widened exactly to binary32, all arithmetic
+ * is binary32 (round to nearest even, subnormals kept) in this order, and the
+ * result is rounded once to the I/O type (nearest even):
+ *     px = fma(dx, offset_scale, (float)(wo*stride - pad + j*dilation)), py alike
+ *     lx = px - floor(px), hx = 1 - lx, ly and hy alike
+ *     w00 = (m*hy)*hx, w01 = (m*hy)*lx, w10 = (m*ly)*hx, w11 = (m*ly)*lx
+ *     per channel, points in order, corners 00, 01, 10, 11: acc = fma(w, v, acc)
+ * so results do not depend on the launch configuration, the vector width,
+ * the alignment of the pointers or the stream.
+ *
+ * All pointers are DEVICE pointers, owned by the caller; the library keeps no
+ * reference after the call returns and allocates no device memory.  Work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ * returns without synchronising: DCNV4_OK means "validated and launched".
+ * Every argument is validated before any HIP call; on an error nothing is
+ * launched and nothing is written.  Calls are thread-safe.
+ */
+#ifndef DCNV4_H
+#define DCNV4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* I/O element type, the same for x, offset, mask and out. */
+typedef enum dcnv4_dtype {
+    DCNV4_F32 = 0,   /* IEEE binary32 */
+    DCNV4_F16 = 1,   /* IEEE binary16 */
+    DCNV4_BF16 = 2   /* bfloat16 (upper half of binary32) */
+} dcnv4_dtype;
+
+typedef enum dcnv4_status {
+    DCNV4_OK = 0,
+    DCNV4_ERR_NULL = 1,       /* a pointer is NULL while there is work to do */
+    DCNV4_ERR_SHAPE = 2,      /* N < 0, or H, W, G or Cg < 1 */
+    DCNV4_ERR_PARAM = 3,      /* K, stride, dilation < 1; pad < 0; Ho or Wo < 1;
+                                 offset_scale not finite; bad remove_center or row stride */
+    DCNV4_ERR_DTYPE = 4,      /* dtype not one of dcnv4_dtype */
+    DCNV4_ERR_ALIAS = 5,      /* out overlaps x, offset or mask */
+    DCNV4_ERR_TOO_LARGE = 6,  /* H or W >= 2^24, one image of x or out >= 2^31
+                                 elements, or N*Ho*Wo*G >= 2^31 */
+    DCNV4_ERR_HIP = 7,        /* no gfx950 device current, or the launch failed */
+    DCNV4_ERR_ALIGN = 8       /* a pointer is not aligned to the element size */
+} dcnv4_status;
+
+/*
+ * The forward operator.
+ *   x       [N, H, W, G*Cg]        input, channels-last, contiguous
+ *   offset  [N, Ho, Wo, G*2*K*K]   per output pixel and group: K*K x-offsets then
+ *                                  K*K y-offsets, in pixels, contiguous
+ *   mask    [N, Ho, Wo, G*K*K]     dynamic weights, raw (no softmax), contiguous
+ *   out     [N, Ho, Wo, G*Cg]      written in full; must not overlap the inputs
+ * N == 0 is a valid no-op.  Returns a dcnv4_status.
+ */
+int dcnv4_forward(const void* x, const void* offset, const void* mask, void* out,
+                  int N, int H, int W, int G, int Cg,
+                  int K, int stride, int pad, int dilation, float offset_scale,
+                  int dtype, void* stream);
+
+/*
+ * The same operator with the two variants the pages name
+ * (pwwt.cn/news/2159231, section "进阶优化建议": dropping the centre point;
+ * jsqmd.com/news/933833, section 2, DCNv4Block example: offsets and weights
+ * predicted together by one projection and split per pixel):
+ *   remove_center  0 or 1; 1 drops point (K/2, K/2), needs odd K >= 3, and
+ *                  P = K*K - 1 points per group are read
+ *   offset_row     elements from one output pixel's offsets to the next
+ *                  (0 = G*2*P, dense); must be >= G*2*P
+ *   mask_row       the same for the weights (0 = G*P); must be >= G*P
+ * With offset = packed, mask = packed + G*2*P and both rows = G*3*P this reads
+ * a packed [N, Ho, Wo, G*3*P] tensor in place.
+ */
+int dcnv4_forward_ex(const void* x, const void* offset, const void* mask, void* out,
+                     int N, int H, int W, int G, int Cg,
+                     int K, int stride, int pad, int dilation, float offset_scale,
+                     int remove_center, int64_t offset_row, int64_t mask_row,
+                     int dtype, void* stream);
+
+/* Ho or Wo for an input extent; <= 0 when the arguments admit no output. */
+int dcnv4_output_dim(int in, int K, int stride, int pad, int dilation);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char* dcnv4_status_string(int status);
+
+/* Details of the last failed call on the calling thread ("" if none). */
+const char* dcnv4_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* dcnv4_version(void);
+
+/*
+ * Launch plan the library would use for these arguments (for reporting):
+ * vector width in elements, lanes per (pixel, group) unit, threads per
+ * block, blocks.  Pure host computation, no HIP call.  Returns a dcnv4_status
+ * from the same validation as the forward call.
+ */
+typedef struct dcnv4_plan {
+    int vec;            /* elements per lane per gather */
+    int lanes_per_unit; /* lanes sharing one (pixel, group) */
+    int block;          /* threads per block */
+    int64_t grid;       /* blocks */
+    int kernel;         /* kernel family id (see dcnv4_kernel_name) */
+} dcnv4_plan;
+
+int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const void* out,
+                     int N, int H, int W, int G, int Cg,
+                     int K, int stride, int pad, int dilation, float offset_scale,
+                     int remove_center, int64_t offset_row, int64_t mask_row,
+                     int dtype, dcnv4_plan* plan);
+
+/* Name of a kernel family id from dcnv4_plan (static text). */
+const char* dcnv4_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCNV4_H */

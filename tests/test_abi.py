@@ -1,0 +1,109 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects every invalid argument before touching HIP (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from deformable_convolution_vision_dcnv4_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcnv4.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE, ERR_ALIAS, ERR_TOO_LARGE, ERR_HIP, ERR_ALIGN = range(9)
+
+# fake, well separated, 256-byte aligned device addresses: validation never dereferences them
+X, OFF, MSK, OUT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcnv4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert re.match(r"^\d+\.\d+\.\d+$", binding.version())
+    for st in range(9):
+        assert binding.status_string(st) not in ("", "unknown status")
+    assert binding.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("n,K,s,p,d", [(16, 3, 1, 1, 1), (7, 3, 2, 0, 1), (5, 3, 1, 2, 2), (2, 5, 1, 0, 1),
+                                       (1, 1, 1, 0, 1), (4, 3, 0, 1, 1), (4, 0, 1, 1, 1)])
+def test_output_dim(n, K, s, p, d):
+    want = (n + 2 * p - d * (K - 1) - 1) // s + 1 if (s >= 1 and K >= 1 and n + 2 * p - d * (K - 1) - 1 >= 0) else 0
+    got = binding.output_dim(n, K, s, p, d)
+    assert (got if got > 0 else 0) == want
+
+
+def call(**kw):
+    a = dict(x=X, off=OFF, msk=MSK, out=OUT, N=2, H=8, W=8, G=4, Cg=16, K=3, s=1, p=1, d=1, scale=1.0,
+             rc=0, orow=0, mrow=0, dtype=1)
+    a.update(kw)
+    L = binding.lib()
+    return L.dcnv4_forward_ex(a["x"], a["off"], a["msk"], a["out"], a["N"], a["H"], a["W"], a["G"],
+                              a["Cg"], a["K"], a["s"], a["p"], a["d"], a["scale"], a["rc"], a["orow"],
+                              a["mrow"], a["dtype"], None)
+
+
+def plan(**kw):
+    a = dict(x=X, off=OFF, msk=MSK, out=OUT, N=2, H=8, W=8, G=4, Cg=16, K=3, s=1, p=1, d=1, scale=1.0,
+             rc=0, orow=0, mrow=0, dtype=1)
+    a.update(kw)
+    pl = binding.Plan()
+    st = binding.lib().dcnv4_query_plan(a["x"], a["off"], a["msk"], a["out"], a["N"], a["H"], a["W"],
+                                        a["G"], a["Cg"], a["K"], a["s"], a["p"], a["d"], a["scale"],
+                                        a["rc"], a["orow"], a["mrow"], a["dtype"], ctypes.byref(pl))
+    return st, pl
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), ERR_DTYPE), (dict(dtype=-1), ERR_DTYPE),
+    (dict(N=-1), ERR_SHAPE), (dict(H=0), ERR_SHAPE), (dict(W=0), ERR_SHAPE), (dict(G=0), ERR_SHAPE),
+    (dict(Cg=0), ERR_SHAPE),
+    (dict(K=0), ERR_PARAM), (dict(s=0), ERR_PARAM), (dict(d=0), ERR_PARAM), (dict(p=-1), ERR_PARAM),
+    (dict(H=1, p=0), ERR_PARAM), (dict(scale=float("inf")), ERR_PARAM),
+    (dict(scale=float("nan")), ERR_PARAM), (dict(rc=2), ERR_PARAM), (dict(rc=1, K=2), ERR_PARAM),
+    (dict(rc=1, K=1, p=0), ERR_PARAM), (dict(orow=71), ERR_PARAM), (dict(mrow=35), ERR_PARAM),
+    (dict(x=0), ERR_NULL), (dict(off=0), ERR_NULL), (dict(msk=0), ERR_NULL), (dict(out=0), ERR_NULL),
+    (dict(x=X + 1), ERR_ALIGN), (dict(out=OUT + 1), ERR_ALIGN), (dict(off=OFF + 2, dtype=0), ERR_ALIGN),
+    (dict(out=X), ERR_ALIAS), (dict(out=OFF + 64), ERR_ALIAS), (dict(out=MSK - 128), ERR_ALIAS),
+    (dict(H=1 << 24), ERR_TOO_LARGE), (dict(H=4096, W=4096, G=16, Cg=16), ERR_TOO_LARGE),
+    (dict(N=1 << 20, H=64, W=64, G=4, Cg=4), ERR_TOO_LARGE),
+])
+def test_invalid_arguments_rejected_before_any_hip_call(kw, status):
+    assert call(**kw) == status
+    assert binding.last_error() != ""
+    assert plan(**kw)[0] == status
+
+
+def test_empty_batch_is_a_noop_even_with_null_pointers():
+    assert call(N=0, x=0, off=0, msk=0, out=0) == OK
+    assert binding.last_error() == ""
+
+
+def test_packed_rows_accepted_by_validation():
+    G, P = 4, 9
+    st, pl = plan(orow=3 * G * P, mrow=3 * G * P, msk=OFF + 2 * G * P * 2)
+    assert st == OK
+
+
+@pytest.mark.parametrize("dtype,Cg,xoff,vec", [(0, 16, 0, 4), (1, 16, 0, 8), (2, 40, 0, 8), (1, 16, 8, 4),
+                                               (1, 16, 4, 2), (1, 16, 2, 1), (0, 3, 0, 1), (2, 6, 0, 2),
+                                               (0, 16, 8, 2)])
+def test_vector_width_follows_alignment_and_cg(dtype, Cg, xoff, vec):
+    st, pl = plan(dtype=dtype, Cg=Cg, x=X + xoff)
+    assert st == OK
+    assert pl.vec == vec
+    assert pl.lanes_per_unit * pl.vec <= Cg and Cg % pl.vec == 0
