@@ -24,8 +24,16 @@ EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_output_dim", "dcnv4_statu
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("vec", ctypes.c_int), ("lanes_per_unit", ctypes.c_int), ("block", ctypes.c_int),
-                ("grid", ctypes.c_int64), ("kernel", ctypes.c_int)]
+    _fields_ = [("kernel", ctypes.c_int), ("vec", ctypes.c_int), ("lanes_per_unit", ctypes.c_int),
+                ("block", ctypes.c_int), ("grid", ctypes.c_int64), ("groups_per_block", ctypes.c_int),
+                ("tile_h", ctypes.c_int), ("tile_w", ctypes.c_int), ("margin_y", ctypes.c_int),
+                ("margin_x", ctypes.c_int), ("window_h", ctypes.c_int), ("window_w", ctypes.c_int),
+                ("full_window", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+    def as_dict(self):
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["kernel"] = lib().dcnv4_kernel_name(self.kernel).decode()
+        return d
 
 
 class DCNv4Error(RuntimeError):
@@ -184,5 +192,4 @@ def query_plan(x, offset, mask, out, *, kernel_size=3, stride=1, pad=1, dilation
                                   stride, pad, dilation, float(offset_scale),
                                   1 if remove_center else 0, orow, mrow, _DTYPE_CODE[x.dtype],
                                   ctypes.byref(pl)))
-    return {"vec": pl.vec, "lanes_per_unit": pl.lanes_per_unit, "block": pl.block, "grid": pl.grid,
-            "kernel": lib().dcnv4_kernel_name(pl.kernel).decode()}
+    return pl.as_dict()

@@ -27,16 +27,23 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def hipcc():
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
 def build(verbose=False, asm_dir=None):
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    cmd = [hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-shared", "-o", LIB + ".tmp"] + sources()
-    if asm_dir:
-        os.makedirs(asm_dir, exist_ok=True)
-        cmd += ["-save-temps=obj"]
+    cmd = [hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-shared", "-o", LIB + ".tmp"] + sources()
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, cwd=asm_dir or CSRC)
+    subprocess.run(cmd, check=True, cwd=CSRC)
     os.replace(LIB + ".tmp", LIB)
+    if asm_dir:
+        # device ISA of each source, for inspection
+        os.makedirs(asm_dir, exist_ok=True)
+        for src in sources():
+            out = os.path.join(asm_dir, os.path.basename(src).replace(".hip", ".s"))
+            subprocess.run([hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "--cuda-device-only",
+                                                    "-S", "-o", out, src], check=True, cwd=CSRC)
     return LIB
 
 

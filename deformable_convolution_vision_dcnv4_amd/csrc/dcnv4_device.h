@@ -1,0 +1,191 @@
+// Device-side building blocks shared by the gfx950 kernels: I/O element
+// types, buffer resources, and the per-point coefficient step of the binary32
+// operation sequence fixed in include/dcnv4.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "dcnv4.h"
+
+#pragma clang fp contract(off)
+
+namespace dcnv4 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Buffer-resource word 3 for gfx950 raw (untyped, stride 0) buffers: 32-bit
+// data format so that out-of-range dwords read as zero.
+constexpr int kRsrcFlags = 0x00020000;
+// A byte offset that is out of range for every resource the kernels build
+// (every resource covers < 2^31 bytes): reads return zeros.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// I/O element types.  to_f widens exactly; from_f rounds to nearest even.
+// ---------------------------------------------------------------------------
+
+template <int DT> struct Elem;
+
+template <> struct Elem<DCNV4_F32> {
+    using S = float;
+    static constexpr int kBytes = 4;
+    static __device__ __forceinline__ float to_f(S v) { return v; }
+    static __device__ __forceinline__ S from_f(float f) { return f; }
+    static __device__ __forceinline__ float raw_to_f(uint32_t r) { return __uint_as_float(r); }
+};
+
+template <> struct Elem<DCNV4_F16> {
+    using S = _Float16;
+    static constexpr int kBytes = 2;
+    static __device__ __forceinline__ float to_f(S v) { return (float)v; }
+    static __device__ __forceinline__ S from_f(float f) { return (S)f; }
+    static __device__ __forceinline__ float raw_to_f(uint32_t r) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)r);
+    }
+};
+
+template <> struct Elem<DCNV4_BF16> {
+    using S = uint16_t;
+    static constexpr int kBytes = 2;
+    static __device__ __forceinline__ float to_f(S v) { return __uint_as_float((uint32_t)v << 16); }
+    static __device__ __forceinline__ S from_f(float f) {
+        uint32_t u = __float_as_uint(f);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return (S)((u >> 16) | 0x40u);   // quiet NaN
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return (S)(u >> 16);
+    }
+    static __device__ __forceinline__ float raw_to_f(uint32_t r) { return __uint_as_float(r << 16); }
+};
+
+// The two bfloat16 halves of a dword widened to binary32 (exact), one
+// v_perm_b32 each.  The byte permute is opaque to the optimiser, so the
+// widening stays next to its multiply-add instead of being hoisted to the
+// load (which would double the registers the loaded data occupies).
+__device__ __forceinline__ float bf16_lo(uint32_t d)
+{
+    return __uint_as_float(__builtin_amdgcn_perm(d, 0u, 0x05040c0cu));   // d << 16
+}
+__device__ __forceinline__ float bf16_hi(uint32_t d)
+{
+    return __uint_as_float(__builtin_amdgcn_perm(d, 0u, 0x07060c0cu));   // d & 0xffff0000
+}
+
+// acc[0..E) += w * (the E elements packed in one 16-byte vector), in element
+// order, one fmaf per element (fp16 folds the widening into the fma).
+template <int DT>
+__device__ __forceinline__ void fma_vec16(float* acc, float w, u32x4 v)
+{
+    if constexpr (DT == DCNV4_F32) {
+        acc[0] = fmaf(w, __uint_as_float(v.x), acc[0]);
+        acc[1] = fmaf(w, __uint_as_float(v.y), acc[1]);
+        acc[2] = fmaf(w, __uint_as_float(v.z), acc[2]);
+        acc[3] = fmaf(w, __uint_as_float(v.w), acc[3]);
+    } else if constexpr (DT == DCNV4_F16) {
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2 h = __builtin_bit_cast(f16x2, d[i]);
+            acc[2 * i] = fmaf(w, (float)h.x, acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, (float)h.y, acc[2 * i + 1]);
+        }
+    } else {
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(w, bf16_lo(d[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, bf16_hi(d[i]), acc[2 * i + 1]);
+        }
+    }
+}
+
+// Elements per 16-byte vector.
+template <int DT> constexpr int kPerVec = 16 / Elem<DT>::kBytes;
+
+// The final binary32 accumulator, made opaque to the optimiser.  Without it
+// the compiler may fuse the last fmaf with the narrowing conversion
+// (v_fma_mixlo_f16): that rounds once, from the exact value, instead of
+// rounding to binary32 first and then to the I/O type, and differs in rare
+// ties.  The asm emits no instruction.
+__device__ __forceinline__ float settle(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Pack E = kPerVec<DT> accumulators into one 16-byte vector of the I/O type.
+template <int DT>
+__device__ __forceinline__ u32x4 pack_vec16(const float* acc_in)
+{
+    using E = Elem<DT>;
+    float acc[kPerVec<DT>];
+#pragma unroll
+    for (int i = 0; i < kPerVec<DT>; ++i) acc[i] = settle(acc_in[i]);
+    u32x4 r;
+    if constexpr (DT == DCNV4_F32) {
+        r.x = __float_as_uint(acc[0]); r.y = __float_as_uint(acc[1]);
+        r.z = __float_as_uint(acc[2]); r.w = __float_as_uint(acc[3]);
+    } else {
+        uint32_t d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, E::from_f(acc[2 * i]));
+            const uint32_t hi = __builtin_bit_cast(uint16_t, E::from_f(acc[2 * i + 1]));
+            d[i] = lo | (hi << 16);
+        }
+        r.x = d[0]; r.y = d[1]; r.z = d[2]; r.w = d[3];
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// One sampling point: position, range test, bilinear weights with the dynamic
+// weight folded in, exactly in the order fixed by the ABI.  A point outside
+// (-1,H) x (-1,W) (or with a NaN coordinate) comes back invalid with all four
+// weights +0 and x0 = y0 = 0, so that it can be routed to zeros.
+// ---------------------------------------------------------------------------
+
+struct PointCoef {
+    float w00, w01, w10, w11;
+    int x0, y0;
+    bool valid;
+};
+
+__device__ __forceinline__ PointCoef point_coef(float dx, float dy, float m, float scale,
+                                                float basex, float basey, float fW, float fH)
+{
+    PointCoef c;
+    float px = fmaf(dx, scale, basex);
+    float py = fmaf(dy, scale, basey);
+    // bitwise & (not &&): no short-circuit, so no branch per point
+    c.valid = (px > -1.0f) & (px < fW) & (py > -1.0f) & (py < fH);
+    px = c.valid ? px : 0.0f;
+    py = c.valid ? py : 0.0f;
+    m = c.valid ? m : 0.0f;
+    const float fx = floorf(px), fy = floorf(py);
+    c.x0 = (int)fx;
+    c.y0 = (int)fy;
+    const float lx = px - fx, ly = py - fy;
+    const float hx = 1.0f - lx, hy = 1.0f - ly;
+    const float mhy = m * hy, mly = m * ly;
+    c.w00 = mhy * hx;
+    c.w01 = mhy * lx;
+    c.w10 = mly * hx;
+    c.w11 = mly * lx;
+    return c;
+}
+
+}  // namespace dcnv4

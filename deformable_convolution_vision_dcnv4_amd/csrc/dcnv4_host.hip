@@ -84,8 +84,14 @@ int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* m
     if (offset_row < dense_off || mask_row < dense_mask)
         return fail(DCNV4_ERR_PARAM, "row strides must be >= G*2*P (%lld) and G*P (%lld)",
                     (long long)dense_off, (long long)dense_mask);
-    if ((int64_t)H * W * C >= ((int64_t)1 << 31) || (int64_t)Ho * Wo * C >= ((int64_t)1 << 31))
-        return fail(DCNV4_ERR_TOO_LARGE, "one image of x or out must hold < 2^31 elements");
+    {
+        // one image of each tensor must span < 2^31 bytes (32-bit buffer offsets)
+        const int64_t s = dtype == DCNV4_F32 ? 4 : 2, lim = (int64_t)1 << 31;
+        const int64_t hw = (int64_t)Ho * Wo;
+        if ((int64_t)H * W * C * s >= lim || hw * C * s >= lim ||
+            ((hw - 1) * offset_row + dense_off) * s >= lim || ((hw - 1) * mask_row + dense_mask) * s >= lim)
+            return fail(DCNV4_ERR_TOO_LARGE, "one image of x, out, offset or mask must span < 2^31 bytes");
+    }
     const int64_t units = (int64_t)N * Ho * Wo * G;
     if (units >= ((int64_t)1 << 31))
         return fail(DCNV4_ERR_TOO_LARGE, "N*Ho*Wo*G must be < 2^31");
@@ -221,18 +227,29 @@ int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const 
     if (st != DCNV4_OK) return st;
     dcnv4::Plan pl;
     dcnv4::make_plan(p, &pl);
+    memset(plan, 0, sizeof *plan);
+    plan->kernel = pl.kernel;
     plan->vec = pl.vec;
     plan->lanes_per_unit = pl.lanes;
     plan->block = pl.block;
     plan->grid = N == 0 ? 0 : pl.grid;
-    plan->kernel = pl.kernel;
+    plan->groups_per_block = pl.GB;
+    plan->tile_h = pl.TH;
+    plan->tile_w = pl.TW;
+    plan->margin_y = pl.RY;
+    plan->margin_x = pl.RX;
+    plan->window_h = pl.WH;
+    plan->window_w = pl.WW;
+    plan->full_window = pl.full;
+    plan->lds_bytes = pl.lds_bytes;
     return DCNV4_OK;
 }
 
 const char* dcnv4_kernel_name(int kernel)
 {
     switch (kernel) {
-        case dcnv4::kKernelGatherVec: return "gather_vec";
+        case dcnv4::kKernelDirect: return "direct";
+        case dcnv4::kKernelWindow: return "window";
         default: return "none";
     }
 }

@@ -1,5 +1,5 @@
-// Internal interface between the ABI layer (dcnv4_host.hip) and the kernels
-// (dcnv4_fwd.hip).  Not installed; the public ABI is include/dcnv4.h.
+// Internal interface between the ABI layer (dcnv4_host.hip) and the launch
+// planner (dcnv4_launch.hip).  Not installed; the public ABI is include/dcnv4.h.
 #pragma once
 
 #include <stdint.h>
@@ -8,8 +8,7 @@
 
 namespace dcnv4 {
 
-// One validated forward problem.  Element strides and counts are in elements
-// of the I/O type.
+// One validated forward problem.  Strides and counts in elements of the I/O type.
 struct Problem {
     const void* x;
     const void* off;
@@ -24,16 +23,23 @@ struct Problem {
 
 enum KernelId {
     kKernelNone = 0,
-    kKernelGatherVec = 1,   // lane per (unit, vector of channels)
+    kKernelDirect = 1,   // corner reads from global memory (general path)
+    kKernelWindow = 2,   // corner reads from an LDS window of x
 };
 
 struct Plan {
     int kernel;
-    int vec;        // elements per lane per gather
+    int vec;        // direct: bytes per lane per corner read
     int lanes;      // lanes per (pixel, group) unit
-    int block;      // threads per block
-    int64_t grid;   // blocks
+    int block;      // threads per workgroup
+    int64_t grid;   // workgroups (before the XCD round-up of the window family)
+    int nv;         // window: 16-byte vectors per unit
+    int GB, TH, TW, RY, RX, WH, WW, full;
+    int lds_bytes;
 };
+
+// Largest LDS allocation one workgroup may use on gfx950 (the CU's 160 KiB).
+constexpr int kLdsPerCu = 160 * 1024;
 
 // Pure host: pick the kernel and launch shape for a validated problem.
 void make_plan(const Problem& p, Plan* plan);

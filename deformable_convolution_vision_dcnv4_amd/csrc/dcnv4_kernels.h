@@ -1,0 +1,73 @@
+// Kernel argument blocks and launch entry points (internal).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dcnv4 {
+
+// Division by a runtime constant d (1 <= d < 2^31) for numerators < 2^31:
+// q = (umulhi(n, mul) + n) >> shift.
+struct FastDiv {
+    uint32_t d, mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    f.shift = l;
+    f.mul = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+    if (d == 1) { f.mul = 0; f.shift = 0; }
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f)
+{
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
+// Shared by every kernel family: one validated problem, in elements of the
+// I/O type unless named *_bytes.
+struct KArgs {
+    const void* x;
+    const void* off;
+    const void* msk;
+    void* out;
+    int H, W, G, Cg, C, K, P, stride, pad, dil, Ho, Wo;
+    int remove_center;
+    int64_t off_row, mask_row;      // elements between output pixels
+    uint32_t img_x_bytes;           // one image of x
+    uint32_t img_off_bytes;         // one image of offsets (rows of its last pixel included)
+    uint32_t img_mask_bytes;
+    int64_t img_x_elems, img_out_elems;
+    int64_t img_off_elems, img_mask_elems;   // image strides of offset / mask (elements)
+    float offset_scale;
+
+    // direct family
+    int lanes;                      // lanes per unit
+    int vec_bytes;                  // bytes per lane per gather
+    uint32_t blocks_per_image;
+    uint32_t units_img;             // Ho*Wo*G
+    FastDiv div_lanes, div_G, div_Wo;
+
+    // window family
+    int GB;                         // groups per workgroup
+    int TH, TW;                     // output tile
+    int RY, RX;                     // window margin beyond the base footprint
+    int WH, WW;                     // window rows / cols held in LDS
+    int pitch;                      // LDS row pitch in 16-byte entries (>= WW + 2, multiple of 16)
+    int slot_bytes;                 // bytes per window pixel = GB*Cg*s
+    int full;                       // window covers [-1,H] x [-1,W]
+    uint32_t tiles_x, tiles_y, gtiles;
+    FastDiv div_GB, div_TW, div_tiles_x, div_tiles_y, div_gtiles, div_CPS, div_pitch;
+    uint32_t lds_bytes;
+};
+
+hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hipStream_t stream);
+hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);
+
+}  // namespace dcnv4

@@ -1,0 +1,277 @@
+// Launch planning for the DCNv4 forward: which kernel family, which tile,
+// which workgroup size.  Pure host code apart from the final launch.
+//
+// Rules (see the kernel files for the why):
+//   window family when K = 3, Cg*s is a whole number of 16-byte vectors (1..5
+//   of them) and x and out are 16-byte aligned.  The groups staged together
+//   (GB) are the fewest whose slice of a pixel fills a 128-byte line, so that
+//   staging and the offset/weight/output rows move whole lines; smaller GB
+//   only when nothing fits.  For that GB, in order of preference:
+//     - the whole zero-bordered image, [-1,H] x [-1,W], if it fits in LDS;
+//     - bands of full-width output rows with a margin of R rows for the
+//       offsets (R = 5 unless tuned), band height chosen to minimise
+//       (rounds of workgroups) x (rows computed + rows staged / 2);
+//     - square tiles;
+//   one workgroup per CU (the window takes most of the 160 KiB), threads per
+//   workgroup the smallest multiple of 64 covering the tile in the fewest passes.
+//   The direct family otherwise.
+// DCNV4_TUNE (environment, read once) overrides the choices for tuning runs:
+// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1".
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "dcnv4.h"
+#include "dcnv4_internal.h"
+#include "dcnv4_kernels.h"
+
+namespace dcnv4 {
+namespace {
+
+struct Tune {
+    int kernel = 0;     // 0 auto, 1 direct, 2 window
+    int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1;
+};
+
+const Tune& tune()
+{
+    static Tune t;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        const char* env = getenv("DCNV4_TUNE");
+        if (!env) return;
+        char buf[256];
+        strncpy(buf, env, sizeof buf - 1);
+        buf[sizeof buf - 1] = '\0';
+        for (char* tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+            char* eq = strchr(tok, '=');
+            if (!eq) continue;
+            *eq = '\0';
+            const char* v = eq + 1;
+            if (!strcmp(tok, "kernel")) t.kernel = !strcmp(v, "direct") ? 1 : !strcmp(v, "window") ? 2 : 0;
+            else if (!strcmp(tok, "gb")) t.gb = atoi(v);
+            else if (!strcmp(tok, "th")) t.th = atoi(v);
+            else if (!strcmp(tok, "tw")) t.tw = atoi(v);
+            else if (!strcmp(tok, "r")) t.r = atoi(v);
+            else if (!strcmp(tok, "block")) t.block = atoi(v);
+            else if (!strcmp(tok, "full")) t.full = atoi(v);
+        }
+    });
+    return t;
+}
+
+int elem_bytes(int dtype) { return dtype == DCNV4_F32 ? 4 : 2; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Window extent (pixels, clamped to the zero-bordered image) for `tile`
+// outputs along one axis with margin r.
+int window_extent(int tile, int stride, int K, int dil, int r, int in)
+{
+    const int64_t e = (int64_t)(tile - 1) * stride + (int64_t)(K - 1) * dil + 2 + 2 * (int64_t)r;
+    return (int)(e < in + 2 ? e : in + 2);
+}
+
+// LDS row pitch (16-byte entries): the window's ww pixels plus at least two
+// zero columns, rounded up to 16 entries so that moving one row down keeps a
+// lane on the same LDS banks.
+int pitch_for(int ww) { return (ww + 2 + 15) / 16 * 16; }
+
+// LDS bytes of a window of GB groups with `unit` bytes per group and pixel.
+int lds_for(int wh, int ww, int slot)
+{
+    return wh * pitch_for(ww) * slot;
+}
+
+// Threads per workgroup for `units` lanes of work: the fewest passes over
+// the units that max_block allows, then the smallest multiple of 64 that
+// covers the units in that many passes.
+int pick_block(int64_t units, int max_block)
+{
+    const int64_t passes = ceil_div(units, max_block);
+    const int64_t b = ceil_div(ceil_div(units, passes), 64) * 64;
+    return (int)(b < 64 ? 64 : b);
+}
+
+bool plan_window(const Problem& p, Plan* pl)
+{
+    const Tune& t = tune();
+    const int s = elem_bytes(p.dtype);
+    if (p.K != 3 || (p.Cg * s) % 16) return false;
+    const int nv = p.Cg * s / 16;
+    if (nv < 1 || nv > 5) return false;
+    if ((uintptr_t)p.x % 16 || (uintptr_t)p.out % 16) return false;
+    const int ub = p.Cg * s;                   // bytes of one group of one pixel
+    const int R = t.r >= 0 ? t.r : 5;          // margin for the offsets, pixels
+    const int cus = 256;
+
+    // group blocks to try: the smallest that fills a 128-byte line first
+    // (full-line staging and coalesced offset/output rows), then smaller
+    int order[64], no = 0;
+    if (t.gb) {
+        if (p.G % t.gb) return false;
+        order[no++] = t.gb;
+    } else {
+        int g0 = p.G;
+        for (int gb = 1; gb <= p.G; ++gb)
+            if (p.G % gb == 0 && gb * ub >= 128) { g0 = gb; break; }
+        for (int gb = g0; gb >= 1 && no < 64; --gb)
+            if (p.G % gb == 0) order[no++] = gb;
+    }
+
+    int GB = 0, TH = 0, TW = 0, WH = 0, WW = 0, full = 0;
+    for (int oi = 0; oi < no && !GB; ++oi) {
+        const int gb = order[oi], slot = gb * ub;
+        // the whole zero-bordered image: no point can leave it
+        if (t.full != 0 && lds_for(p.H + 2, p.W + 2, slot) <= kLdsPerCu) {
+            GB = gb; full = 1; TH = p.Ho; TW = p.Wo; WH = p.H + 2; WW = p.W + 2;
+            break;
+        }
+        if (t.full == 1) continue;
+        // bands of full-width rows
+        const int ww = window_extent(t.tw ? t.tw : p.Wo, p.stride, p.K, p.dil, R, p.W);
+        int max_th = 0;
+        for (int th = 1; th <= p.Ho; ++th) {
+            if (lds_for(window_extent(th, p.stride, p.K, p.dil, R, p.H), ww, slot) > kLdsPerCu) break;
+            max_th = th;
+        }
+        if (t.th) max_th = t.th;
+        if (max_th >= 4 || max_th >= p.Ho) {
+            // band count: fewest rounds of workgroups x (rows computed + half the rows staged)
+            const int nb0 = (int)ceil_div(p.Ho, max_th);
+            double best = 1e30;
+            for (int nb = nb0; nb <= 2 * nb0; ++nb) {
+                const int th = (int)ceil_div(p.Ho, nb);
+                const int64_t wgs = (int64_t)p.N * ceil_div(p.Ho, th) * (p.G / gb);
+                const int64_t rounds = ceil_div(wgs, cus);
+                const double cost = (double)rounds * (th + 0.5 * window_extent(th, p.stride, p.K, p.dil, R, p.H));
+                if (cost < best) { best = cost; TH = th; }
+            }
+            GB = gb; TW = t.tw ? t.tw : p.Wo;
+            break;
+        }
+        // square tiles
+        int best_t = 0;
+        for (int tt = 1; tt <= (p.Ho > p.Wo ? p.Ho : p.Wo); ++tt) {
+            const int wh = window_extent(tt < p.Ho ? tt : p.Ho, p.stride, p.K, p.dil, R, p.H);
+            const int w2 = window_extent(tt < p.Wo ? tt : p.Wo, p.stride, p.K, p.dil, R, p.W);
+            if (lds_for(wh, w2, slot) > kLdsPerCu) break;
+            best_t = tt;
+        }
+        if (best_t >= 4) {
+            GB = gb; TH = best_t < p.Ho ? best_t : p.Ho; TW = best_t < p.Wo ? best_t : p.Wo;
+        }
+    }
+    if (!GB) return false;
+    if (!full) {
+        if (TH > p.Ho) TH = p.Ho;
+        if (TW > p.Wo) TW = p.Wo;
+        WH = window_extent(TH, p.stride, p.K, p.dil, R, p.H);
+        WW = window_extent(TW, p.stride, p.K, p.dil, R, p.W);
+    }
+    const int slot = GB * ub;
+    const int lds = lds_for(WH, WW, slot);
+    if (lds > kLdsPerCu) return false;
+    const int64_t units = (int64_t)TH * TW * GB;
+    const int max_block = nv <= 2 ? 1024 : 512;
+    int block = t.block ? t.block : pick_block(units, max_block);
+    if (block < 64 || block % 64 || block > max_block) block = max_block;
+    if (ceil_div(units, block) > 64) return false;   // the kernel tracks at most 64 passes
+
+    pl->kernel = kKernelWindow;
+    pl->vec = 16;
+    pl->lanes = 1;
+    pl->block = block;
+    pl->nv = nv;
+    pl->GB = GB; pl->TH = TH; pl->TW = TW; pl->RY = full ? 0 : R; pl->RX = full ? 0 : R;
+    pl->WH = WH; pl->WW = WW; pl->full = full;
+    pl->lds_bytes = lds;
+    pl->grid = (int64_t)p.N * ceil_div(p.Ho, TH) * ceil_div(p.Wo, TW) * (p.G / GB);
+    return true;
+}
+
+void plan_direct(const Problem& p, Plan* pl)
+{
+    const int s = elem_bytes(p.dtype);
+    // widest read (<= 16 bytes) that divides the group's channel bytes and
+    // keeps x and out reads/writes aligned
+    int vb = 16;
+    while (vb > s) {
+        if ((p.Cg * s) % vb == 0 && (uintptr_t)p.x % vb == 0 && (uintptr_t)p.out % vb == 0) break;
+        vb >>= 1;
+    }
+    pl->kernel = kKernelDirect;
+    pl->vec = vb;
+    pl->lanes = p.Cg * s / vb;
+    pl->block = 256;
+    pl->nv = 0;
+    pl->GB = pl->TH = pl->TW = pl->RY = pl->RX = pl->WH = pl->WW = pl->full = 0;
+    pl->lds_bytes = 0;
+    const int64_t lanes_img = (int64_t)p.Ho * p.Wo * p.G * pl->lanes;
+    pl->grid = (int64_t)p.N * ceil_div(lanes_img, 256);
+}
+
+}  // namespace
+
+void make_plan(const Problem& p, Plan* plan)
+{
+    const Tune& t = tune();
+    if (t.kernel != 1 && plan_window(p, plan)) return;
+    plan_direct(p, plan);
+}
+
+hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream)
+{
+    const int s = elem_bytes(p.dtype);
+    KArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = p.x; a.off = p.off; a.msk = p.msk; a.out = p.out;
+    a.H = p.H; a.W = p.W; a.G = p.G; a.Cg = p.Cg; a.C = p.G * p.Cg;
+    a.K = p.K; a.P = p.P; a.stride = p.stride; a.pad = p.pad; a.dil = p.dil;
+    a.Ho = p.Ho; a.Wo = p.Wo; a.remove_center = p.remove_center;
+    a.off_row = p.off_row; a.mask_row = p.mask_row;
+    a.offset_scale = p.offset_scale;
+    a.img_x_elems = (int64_t)p.H * p.W * a.C;
+    a.img_out_elems = (int64_t)p.Ho * p.Wo * a.C;
+    a.img_off_elems = (int64_t)p.Ho * p.Wo * p.off_row;
+    a.img_mask_elems = (int64_t)p.Ho * p.Wo * p.mask_row;
+    a.img_x_bytes = (uint32_t)(a.img_x_elems * s);
+    // an image's offset/weight rows end with its last pixel's used elements;
+    // rounded up to whole dwords (a dword holding a used byte is never past
+    // the allocation's last page)
+    a.img_off_bytes = (uint32_t)(((((int64_t)p.Ho * p.Wo - 1) * p.off_row + (int64_t)p.G * 2 * p.P) * s + 3) & ~3ll);
+    a.img_mask_bytes = (uint32_t)(((((int64_t)p.Ho * p.Wo - 1) * p.mask_row + (int64_t)p.G * p.P) * s + 3) & ~3ll);
+
+    if (plan.kernel == kKernelDirect) {
+        a.lanes = plan.lanes;
+        a.vec_bytes = plan.vec;
+        a.units_img = (uint32_t)((int64_t)p.Ho * p.Wo * p.G);
+        a.blocks_per_image = (uint32_t)ceil_div((int64_t)a.units_img * plan.lanes, 256);
+        a.div_lanes = make_fastdiv((uint32_t)plan.lanes);
+        a.div_G = make_fastdiv((uint32_t)p.G);
+        a.div_Wo = make_fastdiv((uint32_t)p.Wo);
+        return launch_direct(a, p.dtype, plan.block, (int64_t)a.blocks_per_image * p.N, stream);
+    }
+    a.GB = plan.GB; a.TH = plan.TH; a.TW = plan.TW; a.RY = plan.RY; a.RX = plan.RX;
+    if (plan.full) a.RY = a.RX = p.H + p.W + 2;   // window origin clamps to (-1, -1)
+    a.WH = plan.WH; a.WW = plan.WW; a.full = plan.full;
+    a.pitch = pitch_for(plan.WW);
+    a.slot_bytes = plan.GB * p.Cg * s;
+    a.tiles_y = (uint32_t)ceil_div(p.Ho, plan.TH);
+    a.tiles_x = (uint32_t)ceil_div(p.Wo, plan.TW);
+    a.gtiles = (uint32_t)(p.G / plan.GB);
+    a.div_GB = make_fastdiv((uint32_t)plan.GB);
+    a.div_TW = make_fastdiv((uint32_t)plan.TW);
+    a.div_tiles_x = make_fastdiv(a.tiles_x);
+    a.div_tiles_y = make_fastdiv(a.tiles_y);
+    a.div_gtiles = make_fastdiv(a.gtiles);
+    a.div_CPS = make_fastdiv((uint32_t)(plan.GB * plan.nv));
+    a.div_pitch = make_fastdiv((uint32_t)a.pitch);
+    a.lds_bytes = (uint32_t)plan.lds_bytes;
+    return launch_window(a, p.dtype, plan.nv, plan.block, plan.grid, stream);
+}
+
+}  // namespace dcnv4

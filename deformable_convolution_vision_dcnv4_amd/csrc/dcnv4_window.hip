@@ -1,0 +1,535 @@
+// DCNv4 forward, "window" kernel family: corner gathers served from LDS.
+//
+// Operation: jsqmd.com/news/933833 ("不只是卷积的平替：我把DCNv4塞进Stable
+// Diffusion的U-Net里"), section 1, code example "DCNv4核心计算流程示例"; the raw,
+// signed dynamic weights of the same section's first optimisation and of
+// bqwf.cn/news/1148139 section 2.1.  Prior art kept from the pages' kernel
+// (jsqmd.com/news/933833 section 1 list; bqwf.cn/news/1148139 section 2.2):
+// one pass fuses sampling, interpolation and aggregation; the group's channels
+// are handled together so each point's bilinear weights are computed once;
+// 16-byte vector accesses.
+//
+// Why LDS: every output (pixel, group) reads 4 corners x K*K points of Cg
+// channels, 36x the bytes of x, at data-dependent addresses.  On gfx950 random
+// 16-byte reads from LDS run several times faster than random global reads
+// that hit L1 or L2, so each workgroup first copies a window of x (its output
+// tile's footprint plus a margin for the offsets) into LDS with coalesced
+// 16-byte loads, then gathers from LDS.  A point whose corners leave the
+// window (a large offset) is read from global memory instead; a window that
+// covers the whole zero-bordered image, [-1,H] x [-1,W], never needs that.
+//
+// Work layout: one workgroup = (image n, GB consecutive groups, TH x TW
+// output tile); one lane = one (pixel, group) unit with all Cg channels, so a
+// point's position and weights are computed once and used for all channels.
+// LDS layout: one plane per (group, 16-byte channel chunk), rows of `pitch`
+// 16-byte entries (pitch a multiple of 16 entries, at least two zero columns
+// right of the window).  Lanes of a wave take consecutive output columns, so
+// the corners they read sit in consecutive entries of one plane: distinct
+// LDS banks except where the offsets scramble them.
+// Workgroups are renumbered so that each XCD (workgroups are dealt to the 8
+// XCDs round-robin) receives a contiguous run of tiles: neighbouring tiles
+// and the groups of one tile share that XCD's L2.
+
+#include "dcnv4_device.h"
+#include "dcnv4_kernels.h"
+
+namespace dcnv4 {
+namespace {
+
+// Load ND consecutive dwords at a 4-byte aligned byte offset: b128 pieces,
+// and the LAST dword always on its own.  Callers may ask for one dword past
+// the data they need (a row that starts 2 bytes into a dword); keeping that
+// dword in a load of its own means no multi-dword load ever straddles the end
+// of a buffer resource, so out-of-range handling only ever zeroes whole
+// unneeded loads.
+template <int ND>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* d)
+{
+    constexpr int NB = ND - 1;        // dwords before the last
+#pragma unroll
+    for (int i = 0; i + 4 <= NB; i += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 4 * i), 0, 0);
+        d[i] = v.x; d[i + 1] = v.y; d[i + 2] = v.z; d[i + 3] = v.w;
+    }
+    d[ND - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * (ND - 1)), 0, 0);
+    constexpr int rem = NB % 4, b = NB - NB % 4;
+    if constexpr (rem == 1) {
+        d[b] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * b), 0, 0);
+    } else if constexpr (rem == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(voff + 4 * b), 0, 0);
+        d[b] = v.x; d[b + 1] = v.y;
+    } else if constexpr (rem == 3) {
+        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)(voff + 4 * b), 0, 0);
+        d[b] = v.x; d[b + 1] = v.y; d[b + 2] = v.z;
+    }
+}
+
+// NE elements of the I/O type starting at byte offset `start` (aligned to the
+// element size), as raw 32-bit containers: element e of a 16-bit type sits in
+// the low (e even) or high (e odd) half of word e/2; a 32-bit type in word e.
+template <int DT, int NE>
+struct RowLoad {
+    static constexpr int kWords = Elem<DT>::kBytes == 4 ? NE : (NE + 1) / 2;
+    uint32_t w[kWords];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t start)
+    {
+        if constexpr (Elem<DT>::kBytes == 4) {
+            load_dwords<NE>(r, start, w);
+        } else {
+            constexpr int ND = (2 * NE + 2 + 3) / 4;      // covers a 2-byte misalignment
+            uint32_t d[ND + 1];
+            load_dwords<ND>(r, start & ~3u, d);
+            d[ND] = 0;
+            const uint32_t sh = (start & 2u) * 8u;        // 0 or 16 bits
+#pragma unroll
+            for (int i = 0; i < kWords; ++i) w[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
+        }
+    }
+
+    __device__ __forceinline__ float get(int e) const
+    {
+        if constexpr (DT == DCNV4_F32) {
+            return __uint_as_float(w[e]);
+        } else if constexpr (DT == DCNV4_F16) {
+            const f16x2 h = __builtin_bit_cast(f16x2, w[e / 2]);
+            return (e & 1) ? (float)h.y : (float)h.x;
+        } else {
+            return (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+        }
+    }
+};
+
+// Decode the renumbered workgroup id into its logical tile index; false for
+// the padding workgroups that round the grid up to a multiple of 8.
+__device__ __forceinline__ bool logical_block(uint32_t b, uint32_t total, uint32_t per_xcd, uint32_t* out)
+{
+    const uint32_t xcd = b & 7u, k = b >> 3;
+    const uint32_t l = xcd * per_xcd + k;
+    *out = l;
+    return k < per_xcd && l < total;
+}
+
+// Corner data and weights of one sampling point, in flight.
+template <int NV>
+struct PointRegs {
+    u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+    float w00, w01, w10, w11;
+};
+
+// Keep the compiler from moving memory operations across this point: bounds
+// the number of sampling points whose corner reads are in flight per lane.
+__device__ __forceinline__ void fence_sched() { asm volatile("" ::: "memory"); }
+
+// Value barrier: the data of a point is taken as produced here, so the
+// optimiser cannot hoist its widening (bf16) above the point's fence and keep
+// both the raw and the widened copies alive.
+template <int NV>
+__device__ __forceinline__ void pin(PointRegs<NV>& r)
+{
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        asm volatile("" : "+v"(r.v00[v]));
+        asm volatile("" : "+v"(r.v01[v]));
+        asm volatile("" : "+v"(r.v10[v]));
+        asm volatile("" : "+v"(r.v11[v]));
+    }
+}
+
+// Per-workgroup constants the point steps need.
+struct WinCtx {
+    const char* lbase;
+    __amdgpu_buffer_rsrc_t rx;
+    float scale, fW, fH;
+    int dil;
+    float wx_lo, wx_hi, wy_lo, wy_hi;   // window test: wx_lo <= px < wx_hi, wy_lo <= py < wy_hi
+    float zx, zy;                       // position of the zero columns (top-left corner)
+    int zxi, zyi;                       // the same as integers
+    int row16;                          // bytes per LDS row (pitch * 16)
+    int plane;                          // bytes per LDS plane
+    int cbase;                          // LDS byte of image pixel (0,0) in plane 0
+    uint32_t row_bytes, pix_bytes;      // global x strides
+    int H, W;
+};
+
+// Point k (grid index q): weights, then the reads of its four corners from
+// the LDS window.  A point that contributes nothing reads the window's zero
+// columns with weight 0.  A valid point whose corners leave a partial window
+// reads the zero columns too and sets `fb`: its whole unit is then
+// recomputed from global memory by unit_global (same operation order).
+template <int DT, int NV, int FULL, int RC, int P>
+__device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
+                                                     const RowLoad<DT, P>& msk, int k, int bx, int by,
+                                                     int ubase, bool& fb)
+{
+    PointRegs<NV> r;
+    const int q = (RC && k >= 4) ? k + 1 : k;
+    const int i = q / 3, j = q % 3;
+    float px = fmaf(offs.get(k), x.scale, (float)(bx + j * x.dil));
+    float py = fmaf(offs.get(P + k), x.scale, (float)(by + i * x.dil));
+    float m = msk.get(k);
+    // bitwise & (not &&): no short-circuit, so no branch per point
+    const bool valid = (px > -1.0f) & (px < x.fW) & (py > -1.0f) & (py < x.fH);
+    bool ok = valid;
+    if (!FULL) {
+        const bool inwin = (px >= x.wx_lo) & (px < x.wx_hi) & (py >= x.wy_lo) & (py < x.wy_hi);
+        ok = valid & inwin;
+        fb = fb | (valid & !inwin);
+    }
+    // a point that reads nothing from the window sits on the zero columns
+    // with weight 0: selecting positions, not addresses, keeps this branch-free
+    px = ok ? px : x.zx;
+    py = ok ? py : x.zy;
+    m = ok ? m : 0.0f;
+    const float fx = floorf(px), fy = floorf(py);
+    const int x0 = (int)fx, y0 = (int)fy;
+    const float lx = px - fx, ly = py - fy;
+    const float hx = 1.0f - lx, hy = 1.0f - ly;
+    const float mhy = m * hy, mly = m * ly;
+    r.w00 = mhy * hx;
+    r.w01 = mhy * lx;
+    r.w10 = mly * hx;
+    r.w11 = mly * lx;
+    const int a00 = __mul24(y0, x.row16) + (x0 << 4) + ubase;
+    const int a10 = a00 + x.row16;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const char* p0 = x.lbase + a00 + v * x.plane;
+        const char* p1 = x.lbase + a10 + v * x.plane;
+        r.v00[v] = *reinterpret_cast<const u32x4*>(p0);
+        r.v01[v] = *reinterpret_cast<const u32x4*>(p0 + 16);
+        r.v10[v] = *reinterpret_cast<const u32x4*>(p1);
+        r.v11[v] = *reinterpret_cast<const u32x4*>(p1 + 16);
+    }
+    return r;
+}
+
+// Per channel, points in order, corners in the order 00, 01, 10, 11.  The
+// accumulators are pinned afterwards: the multiply-adds of this point happen
+// here, not sunk toward the store with the corner data kept alive.
+template <int DT, int NV>
+__device__ __forceinline__ void consume_point(float* acc, const PointRegs<NV>& r)
+{
+    constexpr int EPV = kPerVec<DT>;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        float* ac = acc + v * EPV;
+        fma_vec16<DT>(ac, r.w00, r.v00[v]);
+        fma_vec16<DT>(ac, r.w01, r.v01[v]);
+        fma_vec16<DT>(ac, r.w10, r.v10[v]);
+        fma_vec16<DT>(ac, r.w11, r.v11[v]);
+    }
+#pragma unroll
+    for (int c = 0; c < NV * EPV; ++c) asm volatile("" : "+v"(acc[c]));
+}
+
+// Point k with its corners read from global memory (zero outside the image).
+template <int DT, int NV, int RC, int P>
+__device__ __forceinline__ PointRegs<NV> issue_global(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
+                                                      const RowLoad<DT, P>& msk, int k, int bx, int by,
+                                                      uint32_t gchan)
+{
+    const int q = (RC && k >= 4) ? k + 1 : k;
+    const int i = q / 3, j = q % 3;
+    const PointCoef c = point_coef(offs.get(k), offs.get(P + k), msk.get(k), x.scale,
+                                   (float)(bx + j * x.dil), (float)(by + i * x.dil), x.fW, x.fH);
+    const bool iny0 = c.valid & (c.y0 >= 0), iny1 = c.valid & (c.y0 + 1 < x.H);
+    const bool inx0 = c.x0 >= 0, inx1 = c.x0 + 1 < x.W;
+    const uint32_t b = (uint32_t)c.y0 * x.row_bytes + (uint32_t)c.x0 * x.pix_bytes + gchan;
+    const uint32_t b01 = b + x.pix_bytes, b10 = b + x.row_bytes, b11 = b10 + x.pix_bytes;
+    const uint32_t o00 = (iny0 & inx0) ? b : kOobOffset;
+    const uint32_t o01 = (iny0 & inx1) ? b01 : kOobOffset;
+    const uint32_t o10 = (iny1 & inx0) ? b10 : kOobOffset;
+    const uint32_t o11 = (iny1 & inx1) ? b11 : kOobOffset;
+    PointRegs<NV> r;
+    r.w00 = c.w00; r.w01 = c.w01; r.w10 = c.w10; r.w11 = c.w11;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        r.v00[v] = buf_load16(x.rx, o00 + 16 * v);
+        r.v01[v] = buf_load16(x.rx, o01 + 16 * v);
+        r.v10[v] = buf_load16(x.rx, o10 + 16 * v);
+        r.v11[v] = buf_load16(x.rx, o11 + 16 * v);
+    }
+    return r;
+}
+
+// The whole unit again, every corner read from global memory: the path for
+// units with a point outside a partial window.  Same operation order as the
+// fast path, so the result is the same sequence.  One point at a time: it is
+// rare, and a lean body keeps it from taxing the fast path's registers.
+template <int DT, int NV, int RC, int P>
+__device__ __forceinline__ void unit_global(float* acc, const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
+                                            const RowLoad<DT, P>& msk, int bx, int by, uint32_t gchan)
+{
+    constexpr int NC = NV * kPerVec<DT>;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        PointRegs<NV> r = issue_global<DT, NV, RC, P>(x, offs, msk, k, bx, by, gchan);
+        fence_sched();
+        pin(r);
+        consume_point<DT, NV>(acc, r);
+        fence_sched();
+    }
+}
+
+template <int DT, int NV, int FULL, int RC, int MAXB>
+__global__ void __launch_bounds__(MAXB)
+k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
+{
+    using E = Elem<DT>;
+    constexpr int s = E::kBytes;
+    constexpr int EPV = kPerVec<DT>;          // elements per 16-byte vector
+    constexpr int NC = NV * EPV;              // channels per unit (= Cg)
+    constexpr int P = 9 - RC;                 // points (K = 3)
+    extern __shared__ u32x4 lds[];
+    const uint32_t B = blockDim.x;
+
+    uint32_t lb;
+    if (!logical_block(blockIdx.x, total_blocks, per_xcd, &lb)) return;
+    // logical block = ((n * tiles_y + ty) * tiles_x + tx) * gtiles + gt
+    const uint32_t t1 = fdiv(lb, a.div_gtiles);
+    const uint32_t gt = lb - t1 * a.gtiles;
+    const uint32_t t2 = fdiv(t1, a.div_tiles_x);
+    const uint32_t tx = t1 - t2 * a.tiles_x;
+    const uint32_t n = fdiv(t2, a.div_tiles_y);
+    const uint32_t ty = t2 - n * a.tiles_y;
+
+    const int g0 = (int)gt * a.GB;
+    const int oy0 = (int)ty * a.TH, ox0 = (int)tx * a.TW;
+    const int wy0 = max(-1, oy0 * a.stride - a.pad - a.RY);
+    const int wx0 = max(-1, ox0 * a.stride - a.pad - a.RX);
+    const int wh = min(a.WH, a.H + 1 - wy0);  // window rows inside [-1, H]
+    const int ww = min(a.WW, a.W + 1 - wx0);
+
+    const char* xs = static_cast<const char*>(a.x) + (int64_t)n * a.img_x_elems * s;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs, a.img_x_bytes);
+    const uint32_t pix_bytes = (uint32_t)a.C * s;
+    const uint32_t row_bytes = (uint32_t)a.W * pix_bytes;
+    const uint32_t grp_bytes = (uint32_t)(g0 * a.Cg) * s;
+
+    const char* os_img = static_cast<const char*>(a.off) + (int64_t)n * a.img_off_elems * s;
+    const char* ms_img = static_cast<const char*>(a.msk) + (int64_t)n * a.img_mask_elems * s;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(os_img, a.img_off_bytes);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(ms_img, a.img_mask_bytes);
+    const uint32_t units = (uint32_t)(a.TH * a.TW * a.GB);
+
+    // unit u of this workgroup -> (pixel, group); its offset/weight rows are
+    // prefetched one unit ahead
+    auto unit_of = [&](uint32_t u, int& oy, int& ox, int& gl) {
+        const uint32_t pl = fdiv(u, a.div_GB);
+        gl = (int)(u - pl * (uint32_t)a.GB);
+        const uint32_t oyl = fdiv(pl, a.div_TW);
+        oy = oy0 + (int)oyl;
+        ox = ox0 + (int)(pl - oyl * (uint32_t)a.TW);
+    };
+    auto row_starts = [&](int oy, int ox, int gl, uint32_t& so, uint32_t& sm) {
+        const int64_t pix = (int64_t)oy * a.Wo + ox;
+        const int g = g0 + gl;
+        so = (uint32_t)((pix * a.off_row + (int64_t)g * 2 * P) * s);
+        sm = (uint32_t)((pix * a.mask_row + (int64_t)g * P) * s);
+    };
+
+    RowLoad<DT, 2 * P> offs;
+    RowLoad<DT, P> msk;
+    if (threadIdx.x < units) {
+        // the first unit's rows are requested before the window is staged
+        int oy, ox, gl;
+        unit_of(threadIdx.x, oy, ox, gl);
+        uint32_t so, sm;
+        row_starts(min(oy, a.Ho - 1), min(ox, a.Wo - 1), gl, so, sm);
+        offs.load(ro, so);
+        msk.load(rm, sm);
+    }
+
+    // ---- stage the window.  Chunk c = (window pixel p = c / CPS, chunk
+    // cc = c % CPS of its GB*NV 16-byte chunks), read in that order (pixel-
+    // contiguous in x) and written to plane cc at (row, col) of p.  Columns
+    // from WW to the pitch stay zero, as does everything outside the image.
+    const uint32_t CPS = (uint32_t)a.GB * NV;
+    const uint32_t pitch = (uint32_t)a.pitch;
+    const uint32_t plane16 = (uint32_t)a.WH * pitch;          // entries per plane
+    const uint32_t nchunks = plane16 * CPS;
+    {
+        constexpr int U = 4;
+        for (uint32_t c0 = threadIdx.x; c0 < nchunks; c0 += B * U) {
+            u32x4 v[U];
+            uint32_t dst[U];
+#pragma unroll
+            for (int r = 0; r < U; ++r) {
+                const uint32_t c = c0 + r * B;
+                const uint32_t p = fdiv(c, a.div_CPS);
+                const uint32_t cc = c - p * CPS;
+                const uint32_t wyl = fdiv(p, a.div_pitch);
+                const uint32_t wxl = p - wyl * pitch;
+                const int y = wy0 + (int)wyl, x = wx0 + (int)wxl;
+                const bool in = (c < nchunks) & (wxl < (uint32_t)a.WW) & (y >= 0) & (y < a.H) & (x >= 0) & (x < a.W);
+                const uint32_t voff = (uint32_t)y * row_bytes + (uint32_t)x * pix_bytes + grp_bytes + cc * 16u;
+                const uint32_t o = in ? voff : kOobOffset;
+                v[r] = buf_load16(rx, o);
+                dst[r] = cc * plane16 + p;
+            }
+#pragma unroll
+            for (int r = 0; r < U; ++r) {
+                const uint32_t c = c0 + r * B;
+                if (c < nchunks) lds[dst[r]] = v[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    WinCtx cx;
+    cx.lbase = reinterpret_cast<const char*>(lds);
+    cx.rx = rx;
+    cx.scale = a.offset_scale;
+    cx.fW = (float)a.W;
+    cx.fH = (float)a.H;
+    cx.dil = a.dil;
+    cx.wx_lo = (float)wx0;
+    cx.wx_hi = (float)(wx0 + ww - 1);
+    cx.wy_lo = (float)wy0;
+    cx.wy_hi = (float)(wy0 + wh - 1);
+    cx.zxi = wx0 + a.WW;              // first zero column
+    cx.zyi = wy0;
+    cx.zx = (float)cx.zxi;
+    cx.zy = (float)cx.zyi;
+    cx.row16 = (int)pitch * 16;
+    cx.plane = (int)plane16 * 16;
+    cx.cbase = -(wy0 * (int)pitch + wx0) * 16;
+    cx.row_bytes = row_bytes;
+    cx.pix_bytes = pix_bytes;
+    cx.H = a.H;
+    cx.W = a.W;
+
+    uint32_t u = threadIdx.x;
+    // units whose points leave a partial window, one bit per pass: finished
+    // after the main loop, with every corner read from global memory
+    uint64_t fbmask = 0;
+    for (uint32_t pass = 0; u < units; u += B, ++pass) {
+        int oy, ox, gl;
+        unit_of(u, oy, ox, gl);
+        const RowLoad<DT, 2 * P> co = offs;
+        const RowLoad<DT, P> cm = msk;
+        // the next unit's rows are requested now and land while this unit computes
+        uint32_t nso = 0, nsm = 0;
+        const bool more = u + B < units;
+        if (more) {
+            int oy2, ox2, gl2;
+            unit_of(u + B, oy2, ox2, gl2);
+            row_starts(min(oy2, a.Ho - 1), min(ox2, a.Wo - 1), gl2, nso, nsm);
+            offs.load(ro, nso);
+            msk.load(rm, nsm);
+        }
+        if (oy >= a.Ho || ox >= a.Wo) continue;
+        const int g = g0 + gl;
+
+        float acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
+
+        const int bx = ox * a.stride - a.pad;
+        const int by = oy * a.stride - a.pad;
+        const int ubase = gl * NV * cx.plane + cx.cbase;
+
+        // two points in flight: issue the reads of point k+1, then accumulate point k
+        bool fb = false;
+        PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P>(cx, co, cm, 0, bx, by, ubase, fb);
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            PointRegs<NV> nxt;
+            if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P>(cx, co, cm, k + 1, bx, by, ubase, fb);
+            fence_sched();
+            pin(cur);
+            consume_point<DT, NV>(acc, cur);
+            fence_sched();
+            cur = nxt;
+        }
+        // stored unconditionally (a unit marked in fbmask is recomputed and
+        // stored again below): a store that depended on fb would let the
+        // compiler sink every multiply-add of the unit below the branch and
+        // keep all nine points' corner data alive at once
+        if (!FULL) fbmask |= (uint64_t)fb << pass;
+
+        const int64_t pix = (int64_t)oy * a.Wo + ox;
+        char* op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
+    }
+
+    if (!FULL) {
+        while (fbmask) {
+            const uint32_t pass = (uint32_t)__builtin_ctzll(fbmask);
+            fbmask &= fbmask - 1;
+            int oy, ox, gl;
+            unit_of(threadIdx.x + pass * B, oy, ox, gl);
+            const int g = g0 + gl;
+            uint32_t so, sm;
+            row_starts(oy, ox, gl, so, sm);
+            RowLoad<DT, 2 * P> fo;
+            RowLoad<DT, P> fm;
+            fo.load(ro, so);
+            fm.load(rm, sm);
+            float acc[NC];
+            unit_global<DT, NV, RC, P>(acc, cx, fo, fm, ox * a.stride - a.pad, oy * a.stride - a.pad,
+                                       (uint32_t)(g * a.Cg) * s);
+            const int64_t pix = (int64_t)oy * a.Wo + ox;
+            char* op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
+        }
+    }
+}
+
+template <int NV> constexpr int kMaxBlock = NV <= 2 ? 1024 : 512;
+
+template <int DT, int NV, int FULL, int RC>
+hipError_t launch4(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+{
+    if (block > kMaxBlock<NV> || block < 64 || block % 64) return hipErrorInvalidValue;
+    const uint32_t total = (uint32_t)grid;
+    const uint32_t per_xcd = (total + 7) / 8;
+    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, kMaxBlock<NV>>), dim3(per_xcd * 8), dim3(block),
+                       a.lds_bytes, stream, a, total, per_xcd);
+    return hipGetLastError();
+}
+
+template <int DT, int NV>
+hipError_t launch_nv(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+{
+    if (a.full)
+        return a.remove_center ? launch4<DT, NV, 1, 1>(a, block, grid, stream)
+                               : launch4<DT, NV, 1, 0>(a, block, grid, stream);
+    return a.remove_center ? launch4<DT, NV, 0, 1>(a, block, grid, stream)
+                           : launch4<DT, NV, 0, 0>(a, block, grid, stream);
+}
+
+template <int DT>
+hipError_t launch_dt(const KArgs& a, int nv, int block, int64_t grid, hipStream_t stream)
+{
+    switch (nv) {
+        case 1: return launch_nv<DT, 1>(a, block, grid, stream);
+        case 2: return launch_nv<DT, 2>(a, block, grid, stream);
+        case 3: return launch_nv<DT, 3>(a, block, grid, stream);
+        case 4: return launch_nv<DT, 4>(a, block, grid, stream);
+        case 5: return launch_nv<DT, 5>(a, block, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream)
+{
+    switch (dtype) {
+        case DCNV4_F32: return launch_dt<DCNV4_F32>(a, nv, block, grid, stream);
+        case DCNV4_F16: return launch_dt<DCNV4_F16>(a, nv, block, grid, stream);
+        case DCNV4_BF16: return launch_dt<DCNV4_BF16>(a, nv, block, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dcnv4

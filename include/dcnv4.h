@@ -73,8 +73,8 @@ typedef enum dcnv4_status {
                                  offset_scale not finite; bad remove_center or row stride */
     DCNV4_ERR_DTYPE = 4,      /* dtype not one of dcnv4_dtype */
     DCNV4_ERR_ALIAS = 5,      /* out overlaps x, offset or mask */
-    DCNV4_ERR_TOO_LARGE = 6,  /* H or W >= 2^24, one image of x or out >= 2^31
-                                 elements, or N*Ho*Wo*G >= 2^31 */
+    DCNV4_ERR_TOO_LARGE = 6,  /* H or W >= 2^24, one image of x, out, offset or
+                                 mask spanning >= 2^31 bytes, or N*Ho*Wo*G >= 2^31 */
     DCNV4_ERR_HIP = 7,        /* no gfx950 device current, or the launch failed */
     DCNV4_ERR_ALIGN = 8       /* a pointer is not aligned to the element size */
 } dcnv4_status;
@@ -125,17 +125,21 @@ const char* dcnv4_last_error(void);
 const char* dcnv4_version(void);
 
 /*
- * Launch plan the library would use for these arguments (for reporting):
- * vector width in elements, lanes per (pixel, group) unit, threads per
- * block, blocks.  Pure host computation, no HIP call.  Returns a dcnv4_status
- * from the same validation as the forward call.
+ * Launch plan the library would use for these arguments (for reporting and
+ * tests).  Pure host computation, no HIP call.
  */
 typedef struct dcnv4_plan {
-    int vec;            /* elements per lane per gather */
-    int lanes_per_unit; /* lanes sharing one (pixel, group) */
-    int block;          /* threads per block */
-    int64_t grid;       /* blocks */
-    int kernel;         /* kernel family id (see dcnv4_kernel_name) */
+    int kernel;           /* kernel family id, see dcnv4_kernel_name */
+    int vec;              /* bytes per lane per corner read (direct family) */
+    int lanes_per_unit;   /* lanes sharing one (pixel, group) unit */
+    int block;            /* threads per workgroup */
+    int64_t grid;         /* workgroups */
+    int groups_per_block; /* window family: groups staged together */
+    int tile_h, tile_w;   /* window family: output tile per workgroup */
+    int margin_y, margin_x; /* window family: rows/cols staged beyond the tile footprint */
+    int window_h, window_w; /* window family: staged window (pixels) */
+    int full_window;      /* window family: 1 if the window is the whole zero-bordered image */
+    int lds_bytes;        /* LDS per workgroup */
 } dcnv4_plan;
 
 int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const void* out,

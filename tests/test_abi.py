@@ -99,11 +99,28 @@ def test_packed_rows_accepted_by_validation():
     assert st == OK
 
 
-@pytest.mark.parametrize("dtype,Cg,xoff,vec", [(0, 16, 0, 4), (1, 16, 0, 8), (2, 40, 0, 8), (1, 16, 8, 4),
-                                               (1, 16, 4, 2), (1, 16, 2, 1), (0, 3, 0, 1), (2, 6, 0, 2),
-                                               (0, 16, 8, 2)])
-def test_vector_width_follows_alignment_and_cg(dtype, Cg, xoff, vec):
-    st, pl = plan(dtype=dtype, Cg=Cg, x=X + xoff)
+@pytest.mark.parametrize("dtype,Cg,xoff,K,kernel,vec", [
+    (0, 16, 0, 3, "window", 16), (1, 16, 0, 3, "window", 16), (2, 40, 0, 3, "window", 16),
+    (1, 16, 8, 3, "direct", 8), (1, 16, 4, 3, "direct", 4), (1, 16, 2, 3, "direct", 2),
+    (0, 3, 0, 3, "direct", 4), (2, 6, 0, 3, "direct", 4), (0, 16, 8, 3, "direct", 8),
+    (1, 16, 0, 5, "direct", 16), (1, 128, 0, 3, "direct", 16)])
+def test_plan_kernel_family_and_read_width(dtype, Cg, xoff, K, kernel, vec):
+    st, pl = plan(dtype=dtype, Cg=Cg, x=X + xoff, K=K, p=K // 2)
     assert st == OK
+    d = pl.as_dict()
+    assert d["kernel"] == kernel
     assert pl.vec == vec
-    assert pl.lanes_per_unit * pl.vec <= Cg and Cg % pl.vec == 0
+    s = 4 if dtype == 0 else 2
+    if kernel == "direct":
+        assert pl.lanes_per_unit * pl.vec == Cg * s
+    else:
+        assert pl.lanes_per_unit == 1 and pl.lds_bytes <= 160 * 1024
+        assert pl.window_h >= pl.tile_h + 2 and pl.window_w >= pl.tile_w + 2
+
+
+def test_plan_full_window_for_small_images():
+    # 8x8 image, 4 groups of 16 fp16 channels: the whole zero-bordered image fits
+    st, pl = plan(dtype=1, Cg=16, N=64, H=14, W=14, G=16)
+    assert st == OK and pl.full_window == 1
+    assert (pl.window_h, pl.window_w) == (16, 16)
+    assert pl.grid * pl.groups_per_block == 64 * 16
