@@ -1,20 +1,24 @@
 // Launch planning for the DCNv4 forward: which kernel family, which tile,
 // which workgroup size.  Pure host code apart from the final launch.
 //
-// Rules (see the kernel files for the why):
+// Rules (see the kernel files for the why; the choices were measured on the
+// FlashInternImage-T stage shapes, the 256x256 dense-prediction shape and the
+// 64x64 latent shape):
 //   window family when K = 3, Cg*s is a whole number of 16-byte vectors (1..5
-//   of them) and x and out are 16-byte aligned.  The groups staged together
-//   (GB) are the fewest whose slice of a pixel fills a 128-byte line, so that
-//   staging and the offset/weight/output rows move whole lines; smaller GB
-//   only when nothing fits.  For that GB, in order of preference:
-//     - the whole zero-bordered image, [-1,H] x [-1,W], if it fits in LDS;
-//     - bands of full-width output rows with a margin of R rows for the
-//       offsets (R = 5 unless tuned), band height chosen to minimise
-//       (rounds of workgroups) x (rows computed + rows staged / 2);
-//     - square tiles;
-//   one workgroup per CU (the window takes most of the 160 KiB), threads per
-//   workgroup the smallest multiple of 64 covering the tile in the fewest passes.
-//   The direct family otherwise.
+//   of them) and x and out are 16-byte aligned, and one of these fits:
+//     - the whole zero-bordered image, [-1,H] x [-1,W], for GB groups at
+//       once: the smallest GB whose workgroup has at least 128 units, else
+//       the largest that fits.  No point can leave such a window, and its
+//       workgroups read the fewest bytes per CU; one group per workgroup
+//       measured fastest wherever it fits;
+//     - else bands of full-width output rows with a margin of R rows for the
+//       offsets (R = 5 unless tuned), for the smallest GB, when at most four
+//       bands cover the image: band height chosen to minimise (rounds of
+//       workgroups) x (rows computed + rows staged / 2).  With more bands the
+//       margins cost more staging than LDS saves, and large offsets (whose
+//       units fall back to global reads) make it worse;
+//   threads per workgroup: the smallest multiple of 64 covering the tile in
+//   the fewest passes.  The direct family otherwise.
 // DCNV4_TUNE (environment, read once) overrides the choices for tuning runs:
 // "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1".
 
@@ -108,30 +112,26 @@ bool plan_window(const Problem& p, Plan* pl)
     const int R = t.r >= 0 ? t.r : 5;          // margin for the offsets, pixels
     const int cus = 256;
 
-    // group blocks to try: the smallest that fills a 128-byte line first
-    // (full-line staging and coalesced offset/output rows), then smaller
+    // group blocks to try, smallest first (all divisors of G unless tuned)
     int order[64], no = 0;
-    if (t.gb) {
-        if (p.G % t.gb) return false;
-        order[no++] = t.gb;
-    } else {
-        int g0 = p.G;
-        for (int gb = 1; gb <= p.G; ++gb)
-            if (p.G % gb == 0 && gb * ub >= 128) { g0 = gb; break; }
-        for (int gb = g0; gb >= 1 && no < 64; --gb)
-            if (p.G % gb == 0) order[no++] = gb;
-    }
+    for (int gb = 1; gb <= p.G && no < 64; ++gb)
+        if (p.G % gb == 0 && (!t.gb || gb == t.gb)) order[no++] = gb;
+    if (!no) return false;
 
     int GB = 0, TH = 0, TW = 0, WH = 0, WW = 0, full = 0;
-    for (int oi = 0; oi < no && !GB; ++oi) {
-        const int gb = order[oi], slot = gb * ub;
-        // the whole zero-bordered image: no point can leave it
-        if (t.full != 0 && lds_for(p.H + 2, p.W + 2, slot) <= kLdsPerCu) {
-            GB = gb; full = 1; TH = p.Ho; TW = p.Wo; WH = p.H + 2; WW = p.W + 2;
-            break;
+    // the whole zero-bordered image: no point can leave it
+    if (t.full != 0) {
+        for (int oi = 0; oi < no; ++oi) {
+            const int gb = order[oi];
+            if (lds_for(p.H + 2, p.W + 2, gb * ub) > kLdsPerCu) break;
+            GB = gb;
+            if ((int64_t)p.Ho * p.Wo * gb >= 128) break;
         }
-        if (t.full == 1) continue;
-        // bands of full-width rows
+        if (GB) { full = 1; TH = p.Ho; TW = p.Wo; WH = p.H + 2; WW = p.W + 2; }
+    }
+    // bands of full-width rows
+    for (int oi = 0; oi < no && !GB && t.full != 1; ++oi) {
+        const int gb = order[oi], slot = gb * ub;
         const int ww = window_extent(t.tw ? t.tw : p.Wo, p.stride, p.K, p.dil, R, p.W);
         int max_th = 0;
         for (int th = 1; th <= p.Ho; ++th) {
@@ -139,31 +139,19 @@ bool plan_window(const Problem& p, Plan* pl)
             max_th = th;
         }
         if (t.th) max_th = t.th;
-        if (max_th >= 4 || max_th >= p.Ho) {
-            // band count: fewest rounds of workgroups x (rows computed + half the rows staged)
-            const int nb0 = (int)ceil_div(p.Ho, max_th);
-            double best = 1e30;
-            for (int nb = nb0; nb <= 2 * nb0; ++nb) {
-                const int th = (int)ceil_div(p.Ho, nb);
-                const int64_t wgs = (int64_t)p.N * ceil_div(p.Ho, th) * (p.G / gb);
-                const int64_t rounds = ceil_div(wgs, cus);
-                const double cost = (double)rounds * (th + 0.5 * window_extent(th, p.stride, p.K, p.dil, R, p.H));
-                if (cost < best) { best = cost; TH = th; }
-            }
-            GB = gb; TW = t.tw ? t.tw : p.Wo;
-            break;
+        if (max_th < 1) continue;
+        const int nb0 = (int)ceil_div(p.Ho, max_th);
+        if (nb0 > 4 && !t.th) continue;
+        // band count: fewest rounds of workgroups x (rows computed + half the rows staged)
+        double best = 1e30;
+        for (int nb = nb0; nb <= 2 * nb0; ++nb) {
+            const int th = (int)ceil_div(p.Ho, nb);
+            const int64_t wgs = (int64_t)p.N * ceil_div(p.Ho, th) * (p.G / gb);
+            const int64_t rounds = ceil_div(wgs, cus);
+            const double cost = (double)rounds * (th + 0.5 * window_extent(th, p.stride, p.K, p.dil, R, p.H));
+            if (cost < best) { best = cost; TH = th; }
         }
-        // square tiles
-        int best_t = 0;
-        for (int tt = 1; tt <= (p.Ho > p.Wo ? p.Ho : p.Wo); ++tt) {
-            const int wh = window_extent(tt < p.Ho ? tt : p.Ho, p.stride, p.K, p.dil, R, p.H);
-            const int w2 = window_extent(tt < p.Wo ? tt : p.Wo, p.stride, p.K, p.dil, R, p.W);
-            if (lds_for(wh, w2, slot) > kLdsPerCu) break;
-            best_t = tt;
-        }
-        if (best_t >= 4) {
-            GB = gb; TH = best_t < p.Ho ? best_t : p.Ho; TW = best_t < p.Wo ? best_t : p.Wo;
-        }
+        GB = gb; TW = t.tw ? t.tw : p.Wo;
     }
     if (!GB) return false;
     if (!full) {
