@@ -7,6 +7,7 @@ operator's contract), packed-fp32 instructions disabled, -O3.
 """
 import argparse
 import glob
+import hashlib
 import os
 import subprocess
 
@@ -25,6 +26,21 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def source_hash():
+    """Short digest of the kernel sources and the public header: names a
+    build, so that counter measurements can be matched to the code they
+    were taken on."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(INCLUDE, "dcnv4.h")]
+    for path in files:
+        if not os.path.isfile(path) or path.endswith((".so", ".tmp")):
+            continue
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    h.update(" ".join(HIP_FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def hipcc():

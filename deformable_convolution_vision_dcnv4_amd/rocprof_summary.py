@@ -1,0 +1,149 @@
+"""Summaries of rocprofv3 runs of bench.py, as small text and JSON files.
+
+    python -m deformable_convolution_vision_dcnv4_amd.rocprof_summary \\
+        --workload fiit_stage1 --dtype f16 --stats DIR --fetch DIR --write DIR \\
+        --command "..." --out PREFIX
+
+--stats:  a `rocprofv3 --kernel-trace --stats --output-format csv` directory;
+          the per-kernel table (calls, mean/min/max duration) is kept.
+--fetch:  a `rocprofv3 --pmc FETCH_SIZE --output-format csv` directory;
+--write:  a `rocprofv3 --pmc WRITE_SIZE --output-format csv` directory.
+          Both counters are in KiB per dispatch.  Each is scaled by the
+          factor that makes it read the known size of the plain device-to-
+          device copies bench.py makes of its inputs (the rotating copies:
+          each copies x, offset and mask once, so it reads and writes exactly
+          their bytes).  The scaled bytes per launch of the operator's kernel
+          are its measured HBM traffic.
+Writes PREFIX_kernel_trace.txt and, with the counters, PREFIX_hbm_counters.json
+and PREFIX_hbm_counters.txt, each with the command that produced the data.
+"""
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+from . import build
+from .workloads import WORKLOADS
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+OP_KERNEL_PREFIXES = ("void dcnv4::", "dcnv4::")
+
+
+def _one(pattern):
+    found = sorted(glob.glob(pattern, recursive=True))
+    if not found:
+        raise SystemExit(f"no file matches {pattern}")
+    return found[0]
+
+
+def kernel_stats(d):
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    out = []
+    for r in rows:
+        out.append({"name": r["Name"], "calls": int(r["Calls"]),
+                    "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                    "max_us": float(r["MaxNs"]) / 1e3, "percent": float(r["Percentage"])})
+    return out
+
+
+def counter_rows(d, counter):
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows if r["Counter_Name"] == counter]
+
+
+def is_op(name):
+    return name.startswith(OP_KERNEL_PREFIXES) and ("k_window" in name or "k_direct" in name)
+
+
+def scaled_counter(d, counter, copy_bytes_each):
+    """(KiB per op dispatch, factor, op dispatches, copy dispatches) for one counter."""
+    rows = counter_rows(d, counter)
+    copies = [v for n, v in rows if n.startswith(COPY_KERNEL)]
+    ops = [v for n, v in rows if is_op(n)]
+    if not copies or not ops:
+        raise SystemExit(f"{counter}: {len(copies)} copy and {len(ops)} operator dispatches")
+    # copies come in (x, offset, mask) triples, in that order
+    if len(copies) % 3:
+        raise SystemExit(f"{counter}: {len(copies)} copy dispatches, not a multiple of 3")
+    known = sum(copy_bytes_each[i % 3] for i in range(len(copies)))
+    factor = known / (sum(copies) * 1024.0)
+    return statistics.mean(ops), factor, len(ops), len(copies)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--dtype", required=True)
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--command", required=True, help="the command line of the kernel-trace run")
+    ap.add_argument("--counter-command", default=None,
+                    help="the command line of the counter runs (COUNTER = FETCH_SIZE, then WRITE_SIZE)")
+    ap.add_argument("--out", required=True, help="output path prefix")
+    a = ap.parse_args(argv)
+    wl = WORKLOADS[a.workload]
+    s = {"f32": 4, "f16": 2, "bf16": 2}[a.dtype]
+    Ho, Wo = wl.out_hw()
+    x_b = wl.N * wl.H * wl.W * wl.C * s
+    off_b = wl.N * Ho * Wo * wl.G * 2 * wl.P * s
+    m_b = wl.N * Ho * Wo * wl.G * wl.P * s
+    alg = wl.algorithmic_bytes(a.dtype)
+    def head(cmd):
+        return [f"workload: {wl.describe(a.dtype)}",
+                f"algorithmic bytes per launch: {alg} (x {x_b} + offset {off_b} + mask {m_b} + out {x_b})",
+                f"kernel source hash: {build.source_hash()}",
+                f"command: {cmd}", ""]
+
+    if a.stats:
+        st = kernel_stats(a.stats)
+        lines = head(a.command) + [f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'% time':>7}  kernel"]
+        for r in st:
+            lines.append(f"{r['calls']:6d} {r['avg_us']:10.3f} {r['min_us']:10.3f} {r['max_us']:10.3f} "
+                         f"{r['percent']:7.2f}  {r['name'][:110]}")
+        ops = [r for r in st if is_op(r["name"])]
+        for r in ops:
+            lines.append("")
+            lines.append(f"operator kernel: {r['name']}")
+            lines.append(f"  mean duration {r['avg_us']:.3f} us -> {alg / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s "
+                         f"algorithmic = {alg / (r['avg_us'] * 1e-6) / 8e12 * 100:.1f}% of 8 TB/s")
+        with open(a.out + "_kernel_trace.txt", "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+
+    if a.fetch and a.write:
+        each = (x_b, off_b, m_b)
+        f_kib, f_fac, f_n, f_c = scaled_counter(a.fetch, "FETCH_SIZE", each)
+        w_kib, w_fac, w_n, w_c = scaled_counter(a.write, "WRITE_SIZE", each)
+        fetch_b = f_kib * 1024.0 * f_fac
+        write_b = w_kib * 1024.0 * w_fac
+        ccmd = a.counter_command or a.command
+        rec = {"workload": a.workload, "dtype": a.dtype, "kernel_source_hash": build.source_hash(),
+               "command": ccmd,
+               "fetch_kib_per_dispatch": round(f_kib, 3), "fetch_factor": round(f_fac, 4),
+               "write_kib_per_dispatch": round(w_kib, 3), "write_factor": round(w_fac, 4),
+               "operator_dispatches": [f_n, w_n], "copy_dispatches": [f_c, w_c],
+               "hbm_read_bytes_per_launch": round(fetch_b), "hbm_write_bytes_per_launch": round(write_b),
+               "hbm_bytes_per_launch": round(fetch_b + write_b),
+               "algorithmic_read_bytes": x_b + off_b + m_b, "algorithmic_write_bytes": x_b,
+               "algorithmic_bytes_per_launch": alg}
+        with open(a.out + "_hbm_counters.json", "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        lines = head(ccmd) + [
+            f"FETCH_SIZE: {f_kib:.1f} KiB per operator dispatch (mean of {f_n}); copy calibration "
+            f"factor {f_fac:.4f} ({f_c} copies of known size) -> {fetch_b / 1e6:.2f} MB read "
+            f"(algorithmic {(x_b + off_b + m_b) / 1e6:.2f} MB)",
+            f"WRITE_SIZE: {w_kib:.1f} KiB per operator dispatch (mean of {w_n}); copy calibration "
+            f"factor {w_fac:.4f} -> {write_b / 1e6:.2f} MB written (algorithmic {x_b / 1e6:.2f} MB)",
+            f"HBM traffic per launch: {(fetch_b + write_b) / 1e6:.2f} MB = "
+            f"{(fetch_b + write_b) / alg:.3f} x algorithmic"]
+        with open(a.out + "_hbm_counters.txt", "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
