@@ -28,7 +28,8 @@ class Plan(ctypes.Structure):
                 ("block", ctypes.c_int), ("grid", ctypes.c_int64), ("groups_per_block", ctypes.c_int),
                 ("tile_h", ctypes.c_int), ("tile_w", ctypes.c_int), ("margin_y", ctypes.c_int),
                 ("margin_x", ctypes.c_int), ("window_h", ctypes.c_int), ("window_w", ctypes.c_int),
-                ("full_window", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+                ("full_window", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("coalesced_offsets", ctypes.c_int)]
 
     def as_dict(self):
         d = {name: getattr(self, name) for name, _ in self._fields_}

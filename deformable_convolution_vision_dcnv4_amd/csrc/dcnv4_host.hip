@@ -241,7 +241,8 @@ int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const 
     plan->window_h = pl.WH;
     plan->window_w = pl.WW;
     plan->full_window = pl.full;
-    plan->lds_bytes = pl.lds_bytes;
+    plan->lds_bytes = pl.lds_total;
+    plan->coalesced_offsets = pl.coal;
     return DCNV4_OK;
 }
 

@@ -35,7 +35,9 @@ struct Plan {
     int64_t grid;   // workgroups (before the XCD round-up of the window family)
     int nv;         // window: 16-byte vectors per unit
     int GB, TH, TW, RY, RX, WH, WW, full;
-    int lds_bytes;
+    int coal;       // window: offset rows staged through LDS per wave
+    int lds_bytes;  // dynamic LDS (window)
+    int lds_total;  // all LDS per workgroup (the coalesced variant adds static buffers)
 };
 
 // Largest LDS allocation one workgroup may use on gfx950 (the CU's 160 KiB).

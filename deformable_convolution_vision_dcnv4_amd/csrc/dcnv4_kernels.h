@@ -62,12 +62,21 @@ struct KArgs {
     int pitch;                      // LDS row pitch in 16-byte entries (>= WW + 2, multiple of 16)
     int slot_bytes;                 // bytes per window pixel = GB*Cg*s
     int full;                       // window covers [-1,H] x [-1,W]
+    int coal;                       // offset rows staged through LDS by each wave (GB == 1,
+                                    // full-width tiles, dword-aligned rows)
     uint32_t tiles_x, tiles_y, gtiles;
     FastDiv div_GB, div_TW, div_tiles_x, div_tiles_y, div_gtiles, div_CPS, div_pitch;
-    uint32_t lds_bytes;
+    uint32_t win_bytes;             // LDS of the window (the per-wave offset buffers follow)
+    uint32_t lds_bytes;             // all dynamic LDS
 };
 
 hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hipStream_t stream);
 hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);
+
+// Window kernel limits the planner needs: threads per workgroup it is
+// compiled for, and the LDS of the per-wave offset buffers of its
+// coalesced-offset variant for a workgroup of `block` threads.
+int window_max_block(int nv);
+int window_coal_lds_bytes(int block, int dtype, int P);
 
 }  // namespace dcnv4

@@ -17,10 +17,10 @@
 //       workgroups) x (rows computed + rows staged / 2).  With more bands the
 //       margins cost more staging than LDS saves, and large offsets (whose
 //       units fall back to global reads) make it worse;
-//   threads per workgroup: the smallest multiple of 64 covering the tile in
-//   the fewest passes.  The direct family otherwise.
+//   threads per workgroup: the kernel's maximum, or fewer when one pass covers
+//   the tile.  The direct family otherwise.
 // DCNV4_TUNE (environment, read once) overrides the choices for tuning runs:
-// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1".
+// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1,pitch_add=E,coal=0|1".
 
 #include <stdio.h>
 #include <stdlib.h>
@@ -37,7 +37,7 @@ namespace {
 
 struct Tune {
     int kernel = 0;     // 0 auto, 1 direct, 2 window
-    int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1;
+    int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1, pitch_add = 0, coal = -1;
 };
 
 const Tune& tune()
@@ -62,6 +62,8 @@ const Tune& tune()
             else if (!strcmp(tok, "r")) t.r = atoi(v);
             else if (!strcmp(tok, "block")) t.block = atoi(v);
             else if (!strcmp(tok, "full")) t.full = atoi(v);
+            else if (!strcmp(tok, "pitch_add")) t.pitch_add = atoi(v);
+            else if (!strcmp(tok, "coal")) t.coal = atoi(v);
         }
     });
     return t;
@@ -82,7 +84,7 @@ int window_extent(int tile, int stride, int K, int dil, int r, int in)
 // LDS row pitch (16-byte entries): the window's ww pixels plus at least two
 // zero columns, rounded up to 16 entries so that moving one row down keeps a
 // lane on the same LDS banks.
-int pitch_for(int ww) { return (ww + 2 + 15) / 16 * 16; }
+int pitch_for(int ww) { return (ww + 2 + 15) / 16 * 16 + tune().pitch_add; }
 
 // LDS bytes of a window of GB groups with `unit` bytes per group and pixel.
 int lds_for(int wh, int ww, int slot)
@@ -90,14 +92,14 @@ int lds_for(int wh, int ww, int slot)
     return wh * pitch_for(ww) * slot;
 }
 
-// Threads per workgroup for `units` lanes of work: the fewest passes over
-// the units that max_block allows, then the smallest multiple of 64 that
-// covers the units in that many passes.
+// Threads per workgroup for `units` lanes of work: the most the kernel allows
+// (more waves per CU hide more latency; measured faster than the smallest
+// block with the same number of passes), or the smallest multiple of 64 that
+// covers the units in one pass.
 int pick_block(int64_t units, int max_block)
 {
-    const int64_t passes = ceil_div(units, max_block);
-    const int64_t b = ceil_div(ceil_div(units, passes), 64) * 64;
-    return (int)(b < 64 ? 64 : b);
+    const int64_t b = ceil_div(units, 64) * 64;
+    return (int)(b < max_block ? b : max_block);
 }
 
 bool plan_window(const Problem& p, Plan* pl)
@@ -164,10 +166,20 @@ bool plan_window(const Problem& p, Plan* pl)
     const int lds = lds_for(WH, WW, slot);
     if (lds > kLdsPerCu) return false;
     const int64_t units = (int64_t)TH * TW * GB;
-    const int max_block = nv <= 2 ? 1024 : 512;
+    const int max_block = window_max_block(nv);
     int block = t.block ? t.block : pick_block(units, max_block);
     if (block < 64 || block % 64 || block > max_block) block = max_block;
     if (ceil_div(units, block) > 64) return false;   // the kernel tracks at most 64 passes
+
+    // offset rows through LDS: needs evenly spaced rows of one group (GB = 1,
+    // full-width tiles, rows a whole number of dwords apart) and room for the
+    // per-wave buffers
+    const int s_el = elem_bytes(p.dtype);
+    const bool coal_ok = GB == 1 && TW == p.Wo && (p.off_row * s_el) % 4 == 0 &&
+                         p.off_row * s_el < (1 << 24) &&
+                         lds + window_coal_lds_bytes(block, p.dtype, p.P) <= kLdsPerCu;
+    pl->coal = t.coal == 0 ? 0 : coal_ok ? 1 : 0;
+    pl->lds_total = lds + (pl->coal ? window_coal_lds_bytes(block, p.dtype, p.P) : 0);
 
     pl->kernel = kKernelWindow;
     pl->vec = 16;
@@ -197,6 +209,8 @@ void plan_direct(const Problem& p, Plan* pl)
     pl->block = 256;
     pl->nv = 0;
     pl->GB = pl->TH = pl->TW = pl->RY = pl->RX = pl->WH = pl->WW = pl->full = 0;
+    pl->coal = 0;
+    pl->lds_total = 0;
     pl->lds_bytes = 0;
     const int64_t lanes_img = (int64_t)p.Ho * p.Wo * p.G * pl->lanes;
     pl->grid = (int64_t)p.N * ceil_div(lanes_img, 256);
@@ -245,7 +259,7 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
     }
     a.GB = plan.GB; a.TH = plan.TH; a.TW = plan.TW; a.RY = plan.RY; a.RX = plan.RX;
     if (plan.full) a.RY = a.RX = p.H + p.W + 2;   // window origin clamps to (-1, -1)
-    a.WH = plan.WH; a.WW = plan.WW; a.full = plan.full;
+    a.WH = plan.WH; a.WW = plan.WW; a.full = plan.full; a.coal = plan.coal;
     a.pitch = pitch_for(plan.WW);
     a.slot_bytes = plan.GB * p.Cg * s;
     a.tiles_y = (uint32_t)ceil_div(p.Ho, plan.TH);
@@ -258,7 +272,8 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
     a.div_gtiles = make_fastdiv(a.gtiles);
     a.div_CPS = make_fastdiv((uint32_t)(plan.GB * plan.nv));
     a.div_pitch = make_fastdiv((uint32_t)a.pitch);
-    a.lds_bytes = (uint32_t)plan.lds_bytes;
+    a.win_bytes = (uint32_t)plan.lds_bytes;
+    a.lds_bytes = (uint32_t)plan.lds_total;
     return launch_window(a, p.dtype, plan.nv, plan.block, plan.grid, stream);
 }
 

@@ -68,24 +68,42 @@ __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t v
 // NE elements of the I/O type starting at byte offset `start` (aligned to the
 // element size), as raw 32-bit containers: element e of a 16-bit type sits in
 // the low (e even) or high (e odd) half of word e/2; a 32-bit type in word e.
+// Two steps, so that a row can be requested one unit ahead without waiting
+// for it: issue() starts the loads, finish() (after the data is needed, one
+// pass later) moves a 16-bit row that starts 2 bytes into a dword into place.
 template <int DT, int NE>
 struct RowLoad {
-    static constexpr int kWords = Elem<DT>::kBytes == 4 ? NE : (NE + 1) / 2;
+    static constexpr bool k32 = Elem<DT>::kBytes == 4;
+    static constexpr int kWords = k32 ? NE : (NE + 1) / 2;
+    // dwords loaded (16-bit types: enough to cover a 2-byte misalignment)
+    static constexpr int kLoadDwords = k32 ? NE : (2 * NE + 2 + 3) / 4;
     uint32_t w[kWords];
+    uint32_t raw[k32 ? 1 : kLoadDwords];
+    uint32_t sh;
+
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint32_t start)
+    {
+        if constexpr (k32) {
+            load_dwords<NE>(r, start, w);
+        } else {
+            load_dwords<kLoadDwords>(r, start & ~3u, raw);
+            sh = (start & 2u) * 8u;                       // 0 or 16 bits
+        }
+    }
+
+    __device__ __forceinline__ void finish()
+    {
+        if constexpr (!k32) {
+#pragma unroll
+            for (int i = 0; i < kWords; ++i)
+                w[i] = __builtin_amdgcn_alignbit(i + 1 < kLoadDwords ? raw[i + 1] : 0u, raw[i], sh);
+        }
+    }
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t start)
     {
-        if constexpr (Elem<DT>::kBytes == 4) {
-            load_dwords<NE>(r, start, w);
-        } else {
-            constexpr int ND = (2 * NE + 2 + 3) / 4;      // covers a 2-byte misalignment
-            uint32_t d[ND + 1];
-            load_dwords<ND>(r, start & ~3u, d);
-            d[ND] = 0;
-            const uint32_t sh = (start & 2u) * 8u;        // 0 or 16 bits
-#pragma unroll
-            for (int i = 0; i < kWords; ++i) w[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
-        }
+        issue(r, start);
+        finish();
     }
 
     __device__ __forceinline__ float get(int e) const
@@ -100,6 +118,51 @@ struct RowLoad {
         }
     }
 };
+
+// Offset rows of a wave's 64 consecutive units, moved through LDS.  Per-lane
+// row loads touch 64 different cache lines per instruction (each unit's row
+// is a short piece of a pixel's row of all groups), which the texture path
+// serves several times slower than loads whose lanes walk memory in order.
+// Here piece q = k*64 + lane (k < ND) is dword q % ND of unit q / ND: the
+// lanes of one load cover whole rows dword by dword, and the load unit writes
+// each dword straight to LDS at position q (no registers held while in
+// flight), so unit u's row lands at dwords [u*ND, u*ND + ND) of the wave's
+// buffer, from where its lane reads it back.  `base` = byte offset of the
+// first unit's row; consecutive units' rows are `row_bytes` apart.
+template <int ND>
+__device__ __forceinline__ void stage_offset_rows(__amdgpu_buffer_rsrc_t ro, uint32_t* wbuf, uint32_t lane,
+                                                  uint32_t base, uint32_t row_bytes)
+{
+    // the same for every lane of the wave: a scalar offset
+    base = __builtin_amdgcn_readfirstlane(base);
+    // recomputed at each call (a few integer operations per load) instead of
+    // keeping ND loop-invariant offsets in registers across the whole loop
+    asm volatile("" : "+v"(lane));
+    // (u, d) of piece lane, then stepped by 64 pieces per load
+    uint32_t u = lane / (uint32_t)ND, d = lane - u * (uint32_t)ND;
+    constexpr uint32_t du = 64u / ND, dd = 64u % ND;
+#pragma unroll
+    for (int k = 0; k < ND; ++k) {
+        // u < 64 and a row is < 2^24 bytes (the caller checks): 24-bit multiply
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(wbuf + k * 64),
+                                                 4, (int)(__umul24(u, row_bytes) + 4u * d), (int)base, 0, 0);
+        d += dd;
+        u += du;
+        if (d >= (uint32_t)ND) { d -= ND; ++u; }
+    }
+}
+
+// Wait until this wave's LDS reads have returned (before the load unit may
+// overwrite what they read).
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order).  N <= 15.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
+
+// Buffer loads issued by load_dwords<ND>.
+template <int ND> constexpr int kDwordLoads = (ND - 1) / 4 + ((ND - 1) % 4 != 0) + 1;
 
 // Decode the renumbered workgroup id into its logical tile index; false for
 // the padding workgroups that round the grid up to a multiple of 8.
@@ -275,7 +338,7 @@ __device__ __forceinline__ void unit_global(float* acc, const WinCtx& x, const R
     }
 }
 
-template <int DT, int NV, int FULL, int RC, int MAXB>
+template <int DT, int NV, int FULL, int RC, int COAL, int MAXB>
 __global__ void __launch_bounds__(MAXB)
 k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 {
@@ -284,8 +347,13 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     constexpr int EPV = kPerVec<DT>;          // elements per 16-byte vector
     constexpr int NC = NV * EPV;              // channels per unit (= Cg)
     constexpr int P = 9 - RC;                 // points (K = 3)
+    constexpr int ND = 2 * P * s / 4;         // dwords of one unit's offset row
     extern __shared__ u32x4 lds[];
     const uint32_t B = blockDim.x;
+    const uint32_t lane = threadIdx.x & 63u;
+    // per-wave buffers of the coalesced offset rows, after the window
+    uint32_t* wbuf = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + a.win_bytes) +
+                     (COAL ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64u * ND : 0u);
 
     uint32_t lb;
     if (!logical_block(blockIdx.x, total_blocks, per_xcd, &lb)) return;
@@ -334,15 +402,42 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 
     RowLoad<DT, 2 * P> offs;
     RowLoad<DT, P> msk;
-    if (threadIdx.x < units) {
-        // the first unit's rows are requested before the window is staged
-        int oy, ox, gl;
-        unit_of(threadIdx.x, oy, ox, gl);
-        uint32_t so, sm;
-        row_starts(min(oy, a.Ho - 1), min(ox, a.Wo - 1), gl, so, sm);
-        offs.load(ro, so);
-        msk.load(rm, sm);
+    // coalesced rows: with one group per workgroup and full-width tiles, unit
+    // u of the tile is pixel oy0*Wo + u, so a wave's rows are evenly spaced
+    const uint32_t off_row_bytes = (uint32_t)(a.off_row * s);
+    const uint32_t off_tile_base = (uint32_t)(((int64_t)oy0 * a.Wo * a.off_row + (int64_t)g0 * 2 * P) * s);
+    // linear bookkeeping (coalesced variant): unit u is pixel pix = oy0*Wo + u
+    // of group g0, so moving a lane from unit u to u + B is a few additions
+    // (rows beyond the image read as zeros and are never stored)
+    int lin_oy = 0, lin_ox = 0;
+    uint32_t lin_sm = 0, lin_oo = 0, lin_dox = 0, lin_doy = 0;
+    const uint32_t mask_row_bytes = (uint32_t)(a.mask_row * s);
+    if (COAL) {
+        const uint32_t oyl = fdiv(threadIdx.x, a.div_TW);
+        lin_oy = oy0 + (int)oyl;
+        lin_ox = (int)(threadIdx.x - oyl * (uint32_t)a.Wo);
+        const uint32_t pix = (uint32_t)(oy0 * a.Wo) + threadIdx.x;
+        lin_sm = pix * mask_row_bytes + (uint32_t)(g0 * P * s);
+        lin_oo = (pix * (uint32_t)a.C + (uint32_t)(g0 * a.Cg)) * s;
+        lin_doy = fdiv(B, a.div_TW);
+        lin_dox = B - lin_doy * (uint32_t)a.Wo;
     }
+    // the first unit's offset and weight rows: requested right after the
+    // window's loads (below), so that they queue behind them and stay in
+    // flight across the barrier
+    auto first_rows = [&]() {
+        if (COAL) {
+            stage_offset_rows<ND>(ro, wbuf, lane, off_tile_base + (threadIdx.x - lane) * off_row_bytes, off_row_bytes);
+            if (threadIdx.x < units) msk.issue(rm, lin_sm);
+        } else if (threadIdx.x < units) {
+            int oy, ox, gl;
+            unit_of(threadIdx.x, oy, ox, gl);
+            uint32_t so, sm;
+            row_starts(min(oy, a.Ho - 1), min(ox, a.Wo - 1), gl, so, sm);
+            offs.issue(ro, so);
+            msk.issue(rm, sm);
+        }
+    };
 
     // ---- stage the window.  Chunk c = (window pixel p = c / CPS, chunk
     // cc = c % CPS of its GB*NV 16-byte chunks), read in that order (pixel-
@@ -353,8 +448,11 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     const uint32_t plane16 = (uint32_t)a.WH * pitch;          // entries per plane
     const uint32_t nchunks = plane16 * CPS;
     {
-        constexpr int U = 4;
-        for (uint32_t c0 = threadIdx.x; c0 < nchunks; c0 += B * U) {
+        // U loads per lane in flight before their LDS writes: a whole-image
+        // window of one group (about 7 chunks per lane) is staged in one round
+        constexpr int U = 8;
+        bool rows_issued = false;
+        for (uint32_t c0 = threadIdx.x; c0 < nchunks || !rows_issued; c0 += B * U) {
             u32x4 v[U];
             uint32_t dst[U];
 #pragma unroll
@@ -371,6 +469,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
                 v[r] = buf_load16(rx, o);
                 dst[r] = cc * plane16 + p;
             }
+            if (!rows_issued) {
+                fence_sched();
+                first_rows();
+                fence_sched();
+                rows_issued = true;
+            }
 #pragma unroll
             for (int r = 0; r < U; ++r) {
                 const uint32_t c = c0 + r * B;
@@ -378,7 +482,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             }
         }
     }
-    __syncthreads();
+    // the window's LDS writes are complete and visible to the workgroup; the
+    // first rows' loads may still be in flight (no full memory fence here)
+    wait_lds_reads();
+    fence_sched();
+    __builtin_amdgcn_s_barrier();
+    fence_sched();
 
     WinCtx cx;
     cx.lbase = reinterpret_cast<const char*>(lds);
@@ -409,18 +518,49 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     uint64_t fbmask = 0;
     for (uint32_t pass = 0; u < units; u += B, ++pass) {
         int oy, ox, gl;
-        unit_of(u, oy, ox, gl);
-        const RowLoad<DT, 2 * P> co = offs;
-        const RowLoad<DT, P> cm = msk;
+        if (COAL) {
+            oy = lin_oy; ox = lin_ox; gl = 0;
+        } else {
+            unit_of(u, oy, ox, gl);
+        }
+        RowLoad<DT, 2 * P> co = offs;
+        if (!COAL) co.finish();
+        if (COAL) {
+            // this pass's rows, staged by the wave one pass ahead.  Issued
+            // since then, in this order (the fences keep it): the staging
+            // loads, the weight-row loads (kMaskOps) and the previous unit's
+            // stores (NV); waiting down to the smaller of the last two counts
+            // leaves only later operations in flight
+            constexpr int kMaskOps = kDwordLoads<RowLoad<DT, P>::kLoadDwords>;
+            wait_vmem_at_most<(kMaskOps < NV ? kMaskOps : NV)>();
+            fence_sched();
+#pragma unroll
+            for (int d = 0; d < ND; ++d) co.w[d] = wbuf[lane * ND + d];
+            wait_lds_reads();
+        }
+        RowLoad<DT, P> cm = msk;
+        cm.finish();
         // the next unit's rows are requested now and land while this unit computes
         uint32_t nso = 0, nsm = 0;
         const bool more = u + B < units;
-        if (more) {
+        if (COAL && u - lane + B < units)
+            stage_offset_rows<ND>(ro, wbuf, lane, off_tile_base + (u - lane + B) * off_row_bytes, off_row_bytes);
+        fence_sched();
+        uint32_t oo = 0;
+        if (COAL) {
+            oo = lin_oo;
+            if (more) msk.issue(rm, lin_sm + B * mask_row_bytes);
+            lin_sm += B * mask_row_bytes;
+            lin_oo += B * (uint32_t)a.C * s;
+            lin_ox += (int)lin_dox;
+            lin_oy += (int)lin_doy;
+            if (lin_ox >= a.Wo) { lin_ox -= a.Wo; ++lin_oy; }
+        } else if (more) {
             int oy2, ox2, gl2;
             unit_of(u + B, oy2, ox2, gl2);
             row_starts(min(oy2, a.Ho - 1), min(ox2, a.Wo - 1), gl2, nso, nsm);
-            offs.load(ro, nso);
-            msk.load(rm, nsm);
+            offs.issue(ro, nso);
+            msk.issue(rm, nsm);
         }
         if (oy >= a.Ho || ox >= a.Wo) continue;
         const int g = g0 + gl;
@@ -429,8 +569,8 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
 
-        const int bx = ox * a.stride - a.pad;
-        const int by = oy * a.stride - a.pad;
+        const int bx = __mul24(ox, a.stride) - a.pad;
+        const int by = __mul24(oy, a.stride) - a.pad;
         const int ubase = gl * NV * cx.plane + cx.cbase;
 
         // two points in flight: issue the reads of point k+1, then accumulate point k
@@ -452,8 +592,13 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         // keep all nine points' corner data alive at once
         if (!FULL) fbmask |= (uint64_t)fb << pass;
 
-        const int64_t pix = (int64_t)oy * a.Wo + ox;
-        char* op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s;
+        char* op;
+        if (COAL) {
+            op = static_cast<char*>(a.out) + (int64_t)n * a.img_out_elems * s + oo;
+        } else {
+            const int64_t pix = (int64_t)oy * a.Wo + ox;
+            op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s;
+        }
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
@@ -484,17 +629,35 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     }
 }
 
+}  // namespace
+
+int window_max_block(int nv) { return nv <= 2 ? 1024 : 512; }
+int window_coal_lds_bytes(int block, int dtype, int P)
+{
+    const int s = dtype == DCNV4_F32 ? 4 : 2;
+    return block * (2 * P * s / 4) * 4;
+}
+
+namespace {
+
 template <int NV> constexpr int kMaxBlock = NV <= 2 ? 1024 : 512;
 
-template <int DT, int NV, int FULL, int RC>
-hipError_t launch4(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+template <int DT, int NV, int FULL, int RC, int COAL>
+hipError_t launch5(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
     if (block > kMaxBlock<NV> || block < 64 || block % 64) return hipErrorInvalidValue;
     const uint32_t total = (uint32_t)grid;
     const uint32_t per_xcd = (total + 7) / 8;
-    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, kMaxBlock<NV>>), dim3(per_xcd * 8), dim3(block),
+    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, COAL, kMaxBlock<NV>>), dim3(per_xcd * 8), dim3(block),
                        a.lds_bytes, stream, a, total, per_xcd);
     return hipGetLastError();
+}
+
+template <int DT, int NV, int FULL, int RC>
+hipError_t launch4(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+{
+    return a.coal ? launch5<DT, NV, FULL, RC, 1>(a, block, grid, stream)
+                  : launch5<DT, NV, FULL, RC, 0>(a, block, grid, stream);
 }
 
 template <int DT, int NV>

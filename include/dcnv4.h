@@ -139,7 +139,9 @@ typedef struct dcnv4_plan {
     int margin_y, margin_x; /* window family: rows/cols staged beyond the tile footprint */
     int window_h, window_w; /* window family: staged window (pixels) */
     int full_window;      /* window family: 1 if the window is the whole zero-bordered image */
-    int lds_bytes;        /* LDS per workgroup */
+    int lds_bytes;        /* LDS per workgroup (window and offset-row buffers) */
+    int coalesced_offsets; /* window family: 1 if each wave stages its units' offset rows
+                              through LDS with in-order loads */
 } dcnv4_plan;
 
 int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const void* out,
