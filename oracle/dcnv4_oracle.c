@@ -55,6 +55,18 @@
  *           acc = fmaf(w_ab, v_ab, acc), v_ab = 0 outside the image
  *       accumulating over points in enumeration order, acc starting at +0.
  *
+ *   dcnv4_oracle_backward_f64 -- the gradients of the plain definition
+ *       (triangle-kernel form, below) with respect to x, the offsets and the
+ *       weights, in double precision, written out from the derivative of
+ *       each factor.  The pages name the backward step only as what training
+ *       needs ("不只是卷积的平替" section 4, training; the usage guide's
+ *       module wraps a differentiable op); the derivative itself follows from
+ *       the forward's definition.  Reading where the definition has a kink
+ *       (an integer coordinate, where the bilinear corners change): the
+ *       derivative from the right, which is the one that belongs to the
+ *       corners floor(p) and floor(p)+1 that the forward uses.  Points the
+ *       forward skips have zero gradient.
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
 #include <math.h>
@@ -345,6 +357,111 @@ int dcnv4_oracle_forward_f64(const double* x, const double* offset, const double
                     const double* xv = x + (((int64_t)n * H + qy) * W + qx) * C + (int64_t)g * Cg;
                     for (int c = 0; c < Cg; ++c) o[c] += m * wgt * xv[c];
                 }
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of the plain definition (double precision)                    */
+/* ------------------------------------------------------------------------ */
+
+/* Triangle kernel and its derivative from the right:
+ *   tri(t) = max(0, 1 - |t|);  dtri(t) = -1 for 0 <= t < 1, +1 for -1 <= t < 0,
+ * 0 elsewhere.  A sample at p is sum_q tri(py - qy) tri(px - qx) f(q) over the
+ * integer pixels q of the image, so
+ *   d sample / d f(q) = tri(py - qy) tri(px - qx)
+ *   d sample / d px   = sum_q tri(py - qy) dtri(px - qx) f(q)
+ *   d sample / d py   = sum_q dtri(py - qy) tri(px - qx) f(q)
+ * and out = sum_k m_k sample_k, with p_k = base_k + offset_scale * offset_k. */
+static double tri(double t) { t = fabs(t); return t < 1.0 ? 1.0 - t : 0.0; }
+static double dtri(double t)
+{
+    if (t >= 0.0 && t < 1.0) return -1.0;
+    if (t >= -1.0 && t < 0.0) return 1.0;
+    return 0.0;
+}
+
+/*
+ * grad_out [N,Ho,Wo,G*Cg]; outputs (all double, overwritten):
+ *   grad_x      [N,H,W,G*Cg]
+ *   grad_offset rows of off_stride elements per output pixel (G,2,P used)
+ *   grad_mask   rows of mask_stride elements per output pixel (G,P used)
+ * Optional (may be NULL), for error bounds of a binary32 evaluation:
+ *   abs_x       [N,H,W,G*Cg]  sum of |term| over the terms of grad_x
+ *   cnt_x       [N,H,W,G*Cg]  number of terms of grad_x
+ *   abs_offset  like grad_offset: sum over c and the two corners of each
+ *               difference of |g_c| * weight * (|f(q1)| + |f(q0)|), times |m * scale|
+ *   abs_mask    like grad_mask: sum of |g_c * weight * f(q)|
+ */
+int dcnv4_oracle_backward_f64(const double* x, const double* offset, const double* mask,
+                              const double* grad_out, double* grad_x, double* grad_offset,
+                              double* grad_mask, double* abs_x, double* cnt_x, double* abs_offset,
+                              double* abs_mask, int N, int H, int W, int G, int Cg, int K,
+                              int stride, int pad, int dil, double offset_scale,
+                              int remove_center, int64_t off_stride, int64_t mask_stride)
+{
+    shape_t s;
+    if (make_shape(&s, N, H, W, G, Cg, K, stride, pad, dil, remove_center,
+                   off_stride, mask_stride) != OR_OK)
+        return OR_ERR_ARG;
+    const int64_t C = (int64_t)G * Cg;
+    const int64_t nx = (int64_t)N * H * W * C;
+    for (int64_t i = 0; i < nx; ++i) {
+        grad_x[i] = 0.0;
+        if (abs_x) abs_x[i] = 0.0;
+        if (cnt_x) cnt_x[i] = 0.0;
+    }
+    for (int n = 0; n < N; ++n)
+    for (int ho = 0; ho < s.Ho; ++ho)
+    for (int wo = 0; wo < s.Wo; ++wo) {
+        const int64_t pix = ((int64_t)n * s.Ho + ho) * s.Wo + wo;
+        for (int g = 0; g < G; ++g) {
+            const double* go = grad_out + pix * C + (int64_t)g * Cg;
+            double* gox = grad_offset + pix * s.off_stride + (int64_t)g * 2 * s.P;
+            double* gm = grad_mask + pix * s.mask_stride + (int64_t)g * s.P;
+            int k = 0;
+            for (int i = 0; i < K; ++i)
+            for (int j = 0; j < K; ++j) {
+                if (s.remove_center && i == K / 2 && j == K / 2) continue;
+                const double dx = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + k];
+                const double dy = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + s.P + k];
+                const double m = mask[pix * s.mask_stride + (int64_t)g * s.P + k];
+                const double px = (double)(wo * stride - pad + j * dil) + offset_scale * dx;
+                const double py = (double)(ho * stride - pad + i * dil) + offset_scale * dy;
+                double d_px = 0.0, d_py = 0.0, d_m = 0.0, a_px = 0.0, a_py = 0.0, a_m = 0.0;
+                if (px > -1.0 && px < W && py > -1.0 && py < H) {
+                    const int x0 = (int)floor(px), y0 = (int)floor(py);
+                    for (int qy = y0; qy <= y0 + 1; ++qy)
+                    for (int qx = x0; qx <= x0 + 1; ++qx) {
+                        if (qy < 0 || qy >= H || qx < 0 || qx >= W) continue;
+                        const double ty = tri(py - qy), tx = tri(px - qx);
+                        const double sy = dtri(py - qy), sx = dtri(px - qx);
+                        const int64_t q = (((int64_t)n * H + qy) * W + qx) * C + (int64_t)g * Cg;
+                        for (int c = 0; c < Cg; ++c) {
+                            const double f = x[q + c];
+                            grad_x[q + c] += m * ty * tx * go[c];
+                            if (abs_x) abs_x[q + c] += fabs(m * ty * tx * go[c]);
+                            if (cnt_x) cnt_x[q + c] += 1.0;
+                            d_m += go[c] * ty * tx * f;
+                            d_px += go[c] * ty * sx * f;
+                            d_py += go[c] * sy * tx * f;
+                            a_m += fabs(go[c] * ty * tx * f);
+                            a_px += fabs(go[c] * ty * f);
+                            a_py += fabs(go[c] * tx * f);
+                        }
+                    }
+                }
+                gm[k] = d_m;
+                gox[k] = offset_scale * m * d_px;
+                gox[s.P + k] = offset_scale * m * d_py;
+                if (abs_mask) abs_mask[pix * s.mask_stride + (int64_t)g * s.P + k] = a_m;
+                if (abs_offset) {
+                    abs_offset[pix * s.off_stride + (int64_t)g * 2 * s.P + k] = fabs(offset_scale * m) * a_px;
+                    abs_offset[pix * s.off_stride + (int64_t)g * 2 * s.P + s.P + k] = fabs(offset_scale * m) * a_py;
+                }
+                ++k;
             }
         }
     }

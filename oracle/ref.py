@@ -7,6 +7,7 @@ import this module.  Arrays are host numpy arrays:
     offset  [N, Ho, Wo, G*2*P]       per output pixel, per group (2, P): plane 0
                                      moves along W, plane 1 along H
     mask    [N, Ho, Wo, G*P]         raw dynamic weights (no softmax)
+    grad_out [N, Ho, Wo, G*Cg]       (backward) gradient of the output
 
 with P = K*K, or K*K - 1 when the centre point is removed.  The I/O type is
 named by ``dtype``: "f32" (numpy float32), "f16" (numpy float16) or "bf16"
@@ -43,6 +44,8 @@ def lib():
         L.dcnv4_oracle_forward_f32.restype = i32
         L.dcnv4_oracle_forward_f64.argtypes = [vp, vp, vp, vp] + [i32] * 9 + [f64, i32, i64, i64]
         L.dcnv4_oracle_forward_f64.restype = i32
+        L.dcnv4_oracle_backward_f64.argtypes = [vp] * 11 + [i32] * 9 + [f64, i32, i64, i64]
+        L.dcnv4_oracle_backward_f64.restype = i32
         for name in ("f16_to_f32_array", "bf16_to_f32_array", "f32_to_f16_array", "f32_to_bf16_array"):
             fn = getattr(L, "dcnv4_oracle_" + name)
             fn.argtypes = [vp, vp, i64]
@@ -126,6 +129,39 @@ def forward_f64(x, offset, mask, *, K=3, stride=1, pad=1, dil=1, offset_scale=1.
     if rc != 0:
         raise RuntimeError(f"oracle f64 failed with status {rc}")
     return out
+
+
+def backward_f64(x, offset, mask, grad_out, *, K=3, stride=1, pad=1, dil=1, offset_scale=1.0,
+                 remove_center=False, groups=None, bounds=False):
+    """Gradients of the plain definition in double precision (inputs float64).
+
+    Returns (grad_x [N,H,W,C], grad_offset [N,Ho,Wo,G*2*P], grad_mask
+    [N,Ho,Wo,G*P]).  With ``bounds``, also a dict of the absolute-value sums
+    and term counts that bound a binary32 evaluation's rounding error:
+    {"abs_x", "cnt_x", "abs_offset", "abs_mask"} (same shapes)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    grad_out = np.ascontiguousarray(grad_out, dtype=np.float64)
+    if offset.dtype != np.float64 or mask.dtype != np.float64:
+        raise TypeError("offset/mask must be float64")
+    N, H, W, G, Cg, Ho, Wo, P = _dims(x, offset, mask, K, stride, pad, dil, remove_center, groups)
+    if grad_out.shape != (N, Ho, Wo, G * Cg):
+        raise ValueError("grad_out must be [N, Ho, Wo, G*Cg]")
+    offset = np.ascontiguousarray(offset[..., :G * 2 * P])
+    mask = np.ascontiguousarray(mask[..., :G * P])
+    gx = np.zeros(x.shape, dtype=np.float64)
+    goff = np.zeros((N, Ho, Wo, G * 2 * P), dtype=np.float64)
+    gm = np.zeros((N, Ho, Wo, G * P), dtype=np.float64)
+    null = ctypes.c_void_p(0)
+    extra = [np.zeros_like(gx), np.zeros_like(gx), np.zeros_like(goff), np.zeros_like(gm)] if bounds else None
+    ptrs = [_ptr(e) for e in extra] if bounds else [null] * 4
+    rc = lib().dcnv4_oracle_backward_f64(_ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out), _ptr(gx),
+                                         _ptr(goff), _ptr(gm), *ptrs, N, H, W, G, Cg, K, stride, pad, dil,
+                                         float(offset_scale), int(bool(remove_center)), G * 2 * P, G * P)
+    if rc != 0:
+        raise RuntimeError(f"oracle backward failed with status {rc}")
+    if bounds:
+        return gx, goff, gm, dict(zip(("abs_x", "cnt_x", "abs_offset", "abs_mask"), extra))
+    return gx, goff, gm
 
 
 def to_f32(a, dtype):

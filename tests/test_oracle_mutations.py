@@ -37,6 +37,12 @@ MUTATIONS = {
                             "const double wgt = (1.0 - fabs(py - qy));"),
     "f64_planes_swapped": ("const double dx = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + k];",
                            "const double dx = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + s.P + k];"),
+    "bwd_dtri_sign": ("if (t >= 0.0 && t < 1.0) return -1.0;", "if (t >= 0.0 && t < 1.0) return 1.0;"),
+    "bwd_offset_mask_factor_dropped": ("gox[k] = offset_scale * m * d_px;", "gox[k] = offset_scale * d_px;"),
+    "bwd_offset_planes_swapped": ("gox[k] = offset_scale * m * d_px;", "gox[k] = offset_scale * m * d_py;"),
+    "bwd_scale_dropped": ("gox[s.P + k] = offset_scale * m * d_py;", "gox[s.P + k] = m * d_py;"),
+    "bwd_grad_x_one_axis": ("grad_x[q + c] += m * ty * tx * go[c];", "grad_x[q + c] += m * ty * go[c];"),
+    "bwd_grad_mask_abs": ("d_m += go[c] * ty * tx * f;", "d_m += fabs(go[c]) * ty * tx * f;"),
     "f64_skips_center_always": ("if (s.remove_center && i == K / 2 && j == K / 2) continue;\n                const double dx",
                                 "if (i == K / 2 && j == K / 2) continue;\n                const double dx"),
 }
@@ -54,8 +60,9 @@ def test_planted_mistake_is_caught(name, tmp_path):
     subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC",
                     "-o", str(so), str(csrc), "-lm"], check=True, capture_output=True)
     env = dict(os.environ, DCNV4_ORACLE_LIB=str(so))
+    pins = "test_oracle_backward.py" if name.startswith("bwd_") else "test_oracle_pins.py"
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-W", "ignore::RuntimeWarning",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch '{name}':\n{r.stdout[-2000:]}"
