@@ -19,7 +19,7 @@ F32, F16, BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 # Every symbol include/dcnv4.h declares.
-EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_output_dim", "dcnv4_status_string",
+EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_backward", "dcnv4_output_dim", "dcnv4_status_string",
            "dcnv4_last_error", "dcnv4_version", "dcnv4_query_plan", "dcnv4_kernel_name")
 
 
@@ -56,6 +56,8 @@ def lib():
         L.dcnv4_forward.restype = i32
         L.dcnv4_forward_ex.argtypes = [vp, vp, vp, vp] + [i32] * 9 + [f32, i32, i64, i64, i32, vp]
         L.dcnv4_forward_ex.restype = i32
+        L.dcnv4_backward.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i64, i64, i32, vp]
+        L.dcnv4_backward.restype = i32
         L.dcnv4_output_dim.argtypes = [i32] * 5
         L.dcnv4_output_dim.restype = i32
         L.dcnv4_status_string.argtypes = [i32]
@@ -173,6 +175,51 @@ def forward(x, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1, offs
                                           1 if remove_center else 0, orow, mrow,
                                           _DTYPE_CODE[x.dtype], sptr))
     return out
+
+
+def backward(x, offset, mask, grad_out, *, kernel_size=3, stride=1, pad=1, dilation=1, offset_scale=1.0,
+             remove_center=False, group=None, need=("x", "offset", "mask"), stream=None):
+    """Gradients of `forward` given grad_out = dL/dout [N, Ho, Wo, G*Cg] (x's dtype).
+
+    Returns (grad_x, grad_offset, grad_mask), float32, shaped like x, offset
+    and mask (None for those not in ``need``).  A gradient of an offset/mask
+    view into a packed tensor is returned with the view's row stride (a view
+    into a new packed float32 tensor)."""
+    N, H, W, C, G, K, P = _prepare(x, offset, mask, kernel_size, remove_center, group, None)
+    Ho, Wo = output_dim(H, K, stride, pad, dilation), output_dim(W, K, stride, pad, dilation)
+    if tuple(grad_out.shape) != (N, Ho, Wo, C) or grad_out.dtype != x.dtype or not grad_out.is_contiguous():
+        raise ValueError(f"grad_out must be a contiguous [{N}, {Ho}, {Wo}, {C}] tensor of x's dtype")
+    optr, orow = _row_view(offset, "offset")
+    mptr, mrow = _row_view(mask, "mask")
+    dev = x.device
+    gx = torch.empty(x.shape, dtype=torch.float32, device=dev) if "x" in need else None
+    # gradients of the rows, with the inputs' row strides
+    if orow == mrow and mptr - optr == G * 2 * P * x.element_size() and ("offset" in need or "mask" in need):
+        rows = torch.zeros((N, Ho, Wo, orow), dtype=torch.float32, device=dev)
+        goff_full, gm_full = rows, rows[..., G * 2 * P:]
+    else:
+        goff_full = torch.zeros((N, Ho, Wo, orow), dtype=torch.float32, device=dev) if "offset" in need else None
+        gm_full = torch.zeros((N, Ho, Wo, mrow), dtype=torch.float32, device=dev) if "mask" in need else None
+    if "offset" not in need:
+        goff_full = None
+    if "mask" not in need:
+        gm_full = None
+    if stream is None:
+        with torch.cuda.device(dev):
+            stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+    def ptr(t):
+        return t.data_ptr() if t is not None else None
+
+    with torch.cuda.device(dev):
+        _check(lib().dcnv4_backward(x.data_ptr(), optr, mptr, grad_out.data_ptr(), ptr(gx), ptr(goff_full),
+                                    ptr(gm_full), N, H, W, G, C // G, K, stride, pad, dilation,
+                                    float(offset_scale), 1 if remove_center else 0, orow, mrow,
+                                    _DTYPE_CODE[x.dtype], sptr))
+    goff = goff_full[..., :offset.shape[-1]] if goff_full is not None else None
+    gm = gm_full[..., :mask.shape[-1]] if gm_full is not None else None
+    return gx, goff, gm
 
 
 def forward_raw(x_ptr, offset_ptr, mask_ptr, out_ptr, N, H, W, G, Cg, K, stride, pad, dilation,

@@ -1,0 +1,280 @@
+// DCNv4 backward: gradients of the forward with respect to x, the offsets and
+// the dynamic weights.
+//
+// The forward (jsqmd.com/news/933833, section 1, code example
+// "DCNv4核心计算流程示例"; raw weights per the same section and
+// bqwf.cn/news/1148139 section 2.1) is, per output channel,
+//   out = sum_k m_k * sum_q tri(py_k - qy) tri(px_k - qx) x[q]
+// over the bilinear corners q of point k, with tri(t) = max(0, 1 - |t|) and
+// p_k = base_k + offset_scale * offset_k.  Its gradients, given g = dL/dout:
+//   dL/dx[q]        += m_k * w_q(k) * g                      (scatter)
+//   dL/dm_k          = sum_c g_c * sample_k,c
+//   dL/doffset_x[k]  = offset_scale * m_k * sum_c g_c * (hy (x01 - x00) + ly (x11 - x10))
+//   dL/doffset_y[k]  = offset_scale * m_k * sum_c g_c * (hx (x10 - x00) + lx (x11 - x01))
+// (the derivative from the right at integer coordinates, which belongs to
+// the corners floor(p), floor(p)+1 the forward uses).  Points the forward
+// skips get zero gradient.
+//
+// Layout of the work: as the forward's direct kernel, lanes take (unit,
+// vector) pairs, unit = (pixel, group), L = Cg*s/VB lanes per unit, the L
+// lanes of a unit in one wave.  Per point, each lane forms its channels'
+// partial sums; the unit's first lane adds the L partials in lane order (a
+// fixed order: the offset and weight gradients are reproducible) and writes
+// them.  x's gradient is a scatter: hardware fp32 atomic adds into a buffer
+// this library zeroes first (its summation order is not fixed).
+
+#include <string.h>
+
+#include "dcnv4_device.h"
+#include "dcnv4_internal.h"
+#include "dcnv4_kernels.h"
+
+namespace dcnv4 {
+namespace {
+
+__global__ void __launch_bounds__(256) k_zero_f32(float* __restrict__ p, int64_t n)
+{
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    float4* p4 = reinterpret_cast<float4*>(p);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        p4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = 0.f;
+}
+
+template <int VB>
+__device__ __forceinline__ void load_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* d)
+{
+    if constexpr (VB == 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else if constexpr (VB == 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
+        d[0] = v.x; d[1] = v.y;
+    } else if constexpr (VB == 4) {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+    } else {
+        d[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+    }
+}
+
+// Element i (< VB / s) of a loaded vector, widened to binary32.
+template <int DT>
+__device__ __forceinline__ float elem(const uint32_t* d, int i)
+{
+    if constexpr (DT == DCNV4_F32) {
+        return __uint_as_float(d[i]);
+    } else {
+        const uint32_t w = d[i / 2];
+        return Elem<DT>::raw_to_f((i & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+}
+
+// Sum of v over the L lanes of this lane's unit, in lane order, valid in the
+// unit's first lane (lane0 = that lane's index in the wave).
+__device__ __forceinline__ float unit_sum(float v, int L, int lane0)
+{
+    float s = __shfl(v, lane0);
+    for (int i = 1; i < L; ++i) s += __shfl(v, lane0 + i);
+    return s;
+}
+
+template <int DT, int VB>
+__global__ void __launch_bounds__(256) k_backward(BArgs a)
+{
+    using E = Elem<DT>;
+    using S = typename E::S;
+    constexpr int s = E::kBytes;
+    constexpr int NE = VB / s;                 // channels per lane
+    constexpr int NW = (VB + 3) / 4;           // dwords per vector
+
+    // block = 4 waves; a wave holds upw units of L lanes (the rest idle)
+    const int L = a.lanes;
+    const int upw = a.units_per_wave;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int uiw = lane / L;                  // unit in wave
+    const int lane_in_unit = lane - uiw * L;
+    const int64_t ublk = (int64_t)blockIdx.x * 4 * upw;
+    const int64_t unit_g = ublk + (int64_t)wave * upw + uiw;
+    const bool active = uiw < upw && unit_g < a.units_total;
+    const int lane0 = uiw * L;
+
+    // unit -> (n, ho, wo, g); inactive lanes take unit 0 (all loads in range)
+    const uint32_t u = active ? (uint32_t)unit_g : 0u;
+    const uint32_t n = fdiv(u, a.div_units_img);
+    const uint32_t ui = u - n * a.units_img;
+    const uint32_t pix = fdiv(ui, a.div_G);
+    const uint32_t g = ui - pix * (uint32_t)a.G;
+    const uint32_t ho = fdiv(pix, a.div_Wo);
+    const uint32_t wo = pix - ho * (uint32_t)a.Wo;
+
+    const char* xs = static_cast<const char*>(a.x) + (int64_t)n * a.img_x_elems * s;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs, a.img_x_bytes);
+    const S* os = static_cast<const S*>(a.off) + (int64_t)n * a.img_off_elems + (int64_t)pix * a.off_row + g * 2 * a.P;
+    const S* ms = static_cast<const S*>(a.msk) + (int64_t)n * a.img_mask_elems + (int64_t)pix * a.mask_row + g * a.P;
+    const uint32_t chan = g * (uint32_t)a.Cg + (uint32_t)(lane_in_unit * NE);
+    const uint32_t pix_bytes = (uint32_t)a.C * s;
+    const uint32_t row_bytes = (uint32_t)a.W * pix_bytes;
+
+    // this lane's channels of the output gradient
+    float gr[NE];
+    {
+        const S* gp = static_cast<const S*>(a.gout) + (int64_t)n * a.img_out_elems + (int64_t)pix * a.C + chan;
+#pragma unroll
+        for (int c = 0; c < NE; ++c) gr[c] = E::to_f(gp[c]);
+    }
+    float* gxi = a.gx ? a.gx + (int64_t)n * a.img_x_elems : nullptr;
+
+    const float fW = (float)a.W, fH = (float)a.H;
+    const int bx0 = (int)wo * a.stride - a.pad;
+    const int by0 = (int)ho * a.stride - a.pad;
+    const int K = a.K, KK = K * K, center = KK / 2;
+    int k = 0;
+    for (int q = 0; q < KK; ++q) {
+        if (a.remove_center && q == center) continue;
+        const int i = q / K, j = q - (q / K) * K;
+        const float dx = E::to_f(os[k]), dy = E::to_f(os[a.P + k]), m = E::to_f(ms[k]);
+        float px = fmaf(dx, a.offset_scale, (float)(bx0 + j * a.dil));
+        float py = fmaf(dy, a.offset_scale, (float)(by0 + i * a.dil));
+        const bool valid = (px > -1.0f) & (px < fW) & (py > -1.0f) & (py < fH);
+        px = valid ? px : 0.0f;
+        py = valid ? py : 0.0f;
+        const float fx = floorf(px), fy = floorf(py);
+        const int x0 = (int)fx, y0 = (int)fy;
+        const float lx = px - fx, ly = py - fy;
+        const float hx = 1.0f - lx, hy = 1.0f - ly;
+
+        const bool iny0 = valid & (y0 >= 0), iny1 = valid & (y0 + 1 < a.H);
+        const bool inx0 = x0 >= 0, inx1 = x0 + 1 < a.W;
+        const uint32_t base = (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + chan * s;
+        const uint32_t b01 = base + pix_bytes, b10 = base + row_bytes, b11 = b10 + pix_bytes;
+        uint32_t d00[NW], d01[NW], d10[NW], d11[NW];
+        load_vec<VB>(rx, (iny0 & inx0) ? base : kOobOffset, d00);
+        load_vec<VB>(rx, (iny0 & inx1) ? b01 : kOobOffset, d01);
+        load_vec<VB>(rx, (iny1 & inx0) ? b10 : kOobOffset, d10);
+        load_vec<VB>(rx, (iny1 & inx1) ? b11 : kOobOffset, d11);
+
+        float sm = 0.0f, sx = 0.0f, sy = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NE; ++c) {
+            const float v00 = elem<DT>(d00, c), v01 = elem<DT>(d01, c);
+            const float v10 = elem<DT>(d10, c), v11 = elem<DT>(d11, c);
+            const float bil = hy * (hx * v00 + lx * v01) + ly * (hx * v10 + lx * v11);
+            const float ddx = hy * (v01 - v00) + ly * (v11 - v10);
+            const float ddy = hx * (v10 - v00) + lx * (v11 - v01);
+            sm += gr[c] * bil;
+            sx += gr[c] * ddx;
+            sy += gr[c] * ddy;
+        }
+
+        // x's gradient: the forward's weights (m folded in) times g, per corner inside
+        if (gxi && active && valid) {
+            const float mhy = m * hy, mly = m * ly;
+            const float w[4] = {mhy * hx, mhy * lx, mly * hx, mly * lx};
+            const bool in[4] = {(bool)(iny0 & inx0), (bool)(iny0 & inx1), (bool)(iny1 & inx0), (bool)(iny1 & inx1)};
+            const uint32_t off[4] = {base, b01, b10, b11};
+#pragma unroll
+            for (int cr = 0; cr < 4; ++cr) {
+                if (!in[cr]) continue;
+                float* dst = gxi + off[cr] / s;
+#pragma unroll
+                for (int c = 0; c < NE; ++c) unsafeAtomicAdd(dst + c, w[cr] * gr[c]);
+            }
+        }
+
+        // the unit's sums, in lane order, by its first lane
+        const float tm = unit_sum(sm, L, lane0);
+        const float tx = unit_sum(sx, L, lane0);
+        const float ty = unit_sum(sy, L, lane0);
+        if (active && lane_in_unit == 0) {
+            const float ms_ = valid ? a.offset_scale * m : 0.0f;
+            const int64_t prow = (int64_t)n * a.img_off_elems + (int64_t)pix * a.off_row + g * 2 * a.P;
+            const int64_t mrow = (int64_t)n * a.img_mask_elems + (int64_t)pix * a.mask_row + g * a.P;
+            if (a.goff) {
+                a.goff[prow + k] = valid ? ms_ * tx : 0.0f;
+                a.goff[prow + a.P + k] = valid ? ms_ * ty : 0.0f;
+            }
+            if (a.gmask) a.gmask[mrow + k] = valid ? tm : 0.0f;
+        }
+        ++k;
+    }
+}
+
+template <int DT>
+hipError_t launch_dt(const BArgs& a, int64_t grid, hipStream_t stream)
+{
+    switch (a.vec_bytes) {
+        case 16: hipLaunchKernelGGL((k_backward<DT, 16>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((k_backward<DT, 8>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((k_backward<DT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+        case 2:
+            if constexpr (DT != DCNV4_F32) {
+                hipLaunchKernelGGL((k_backward<DT, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+                break;
+            }
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int backward_vec_bytes(const Problem& p, const void* gout)
+{
+    const int s = p.dtype == DCNV4_F32 ? 4 : 2;
+    int vb = 16;
+    while (vb > s) {
+        if ((p.Cg * s) % vb == 0 && (uintptr_t)p.x % vb == 0 && (uintptr_t)gout % vb == 0) break;
+        vb >>= 1;
+    }
+    return vb;
+}
+
+hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
+                           hipStream_t stream)
+{
+    const int s = p.dtype == DCNV4_F32 ? 4 : 2;
+    BArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = p.x; a.off = p.off; a.msk = p.msk; a.gout = gout;
+    a.gx = gx; a.goff = goff; a.gmask = gmask;
+    a.H = p.H; a.W = p.W; a.G = p.G; a.Cg = p.Cg; a.C = p.G * p.Cg;
+    a.K = p.K; a.P = p.P; a.stride = p.stride; a.pad = p.pad; a.dil = p.dil;
+    a.Ho = p.Ho; a.Wo = p.Wo; a.remove_center = p.remove_center;
+    a.off_row = p.off_row; a.mask_row = p.mask_row;
+    a.offset_scale = p.offset_scale;
+    a.img_x_elems = (int64_t)p.H * p.W * a.C;
+    a.img_out_elems = (int64_t)p.Ho * p.Wo * a.C;
+    a.img_off_elems = (int64_t)p.Ho * p.Wo * p.off_row;
+    a.img_mask_elems = (int64_t)p.Ho * p.Wo * p.mask_row;
+    a.img_x_bytes = (uint32_t)(a.img_x_elems * s);
+    a.vec_bytes = backward_vec_bytes(p, gout);
+    a.lanes = p.Cg * s / a.vec_bytes;
+    a.units_per_wave = 64 / a.lanes;
+    a.units_img = (uint32_t)((int64_t)p.Ho * p.Wo * p.G);
+    a.units_total = (int64_t)p.N * a.units_img;
+    a.div_units_img = make_fastdiv(a.units_img);
+    a.div_G = make_fastdiv((uint32_t)p.G);
+    a.div_Wo = make_fastdiv((uint32_t)p.Wo);
+
+    if (gx) {
+        const int64_t n = (int64_t)p.N * a.img_x_elems;
+        const int64_t blocks = ceil_div(ceil_div(n, 4), 256);
+        hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, gx, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t grid = ceil_div(a.units_total, 4 * (int64_t)a.units_per_wave);
+    switch (p.dtype) {
+        case DCNV4_F32: return launch_dt<DCNV4_F32>(a, grid, stream);
+        case DCNV4_F16: return launch_dt<DCNV4_F16>(a, grid, stream);
+        case DCNV4_BF16: return launch_dt<DCNV4_BF16>(a, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dcnv4

@@ -46,11 +46,13 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-// Validate and fill a Problem.  Returns DCNV4_OK or an error status.
+// Validate and fill a Problem.  Returns DCNV4_OK or an error status.  With
+// check_pointers false only the shapes and parameters are checked (the
+// backward checks its own pointers).
 int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* mask,
              const void* out, int N, int H, int W, int G, int Cg, int K, int stride,
              int pad, int dil, float offset_scale, int remove_center,
-             int64_t offset_row, int64_t mask_row, int dtype)
+             int64_t offset_row, int64_t mask_row, int dtype, bool check_pointers = true)
 {
     g_last_error[0] = '\0';
     if (dtype != DCNV4_F32 && dtype != DCNV4_F16 && dtype != DCNV4_BF16)
@@ -101,7 +103,7 @@ int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* m
     p->stride = stride; p->pad = pad; p->dil = dil; p->Ho = Ho; p->Wo = Wo;
     p->remove_center = remove_center; p->off_row = offset_row; p->mask_row = mask_row;
     p->offset_scale = offset_scale; p->dtype = dtype;
-    if (N == 0) return DCNV4_OK;
+    if (N == 0 || !check_pointers) return DCNV4_OK;
 
     if (!x || !offset || !mask || !out)
         return fail(DCNV4_ERR_NULL, "null pointer (x=%p offset=%p mask=%p out=%p)", x, offset, mask, out);
@@ -166,9 +168,75 @@ int forward_impl(const void* x, const void* offset, const void* mask, void* out,
     return DCNV4_OK;
 }
 
+int backward_impl(const void* x, const void* offset, const void* mask, const void* grad_out,
+                  float* grad_x, float* grad_offset, float* grad_mask,
+                  int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,
+                  float offset_scale, int remove_center, int64_t offset_row, int64_t mask_row,
+                  int dtype, void* stream)
+{
+    dcnv4::Problem p;
+    int st = validate(&p, x, offset, mask, nullptr, N, H, W, G, Cg, K, stride, pad, dil,
+                      offset_scale, remove_center, offset_row, mask_row, dtype, false);
+    if (st != DCNV4_OK) return st;
+    {
+        // binary32 gradients: one image of grad_x, grad_offset, grad_mask < 2^31 bytes
+        const int64_t lim = (int64_t)1 << 31, hw = (int64_t)p.Ho * p.Wo;
+        const int64_t C = (int64_t)G * Cg;
+        if ((int64_t)H * W * C * 4 >= lim || ((hw - 1) * p.off_row + (int64_t)G * 2 * p.P) * 4 >= lim ||
+            ((hw - 1) * p.mask_row + (int64_t)G * p.P) * 4 >= lim)
+            return fail(DCNV4_ERR_TOO_LARGE, "one image of a binary32 gradient must span < 2^31 bytes");
+    }
+    if (N == 0) return DCNV4_OK;
+    if (!x || !offset || !mask || !grad_out)
+        return fail(DCNV4_ERR_NULL, "null input pointer (x=%p offset=%p mask=%p grad_out=%p)", x, offset, mask,
+                    grad_out);
+    const int s = dtype == DCNV4_F32 ? 4 : 2;
+    if ((uintptr_t)x % s || (uintptr_t)offset % s || (uintptr_t)mask % s || (uintptr_t)grad_out % s ||
+        (uintptr_t)grad_x % 4 || (uintptr_t)grad_offset % 4 || (uintptr_t)grad_mask % 4)
+        return fail(DCNV4_ERR_ALIGN, "inputs must be aligned to %d bytes and gradients to 4", s);
+    if (dcnv4::backward_vec_bytes(p, grad_out) * 64 < Cg * s)
+        return fail(DCNV4_ERR_TOO_LARGE, "the backward handles up to 64 vectors per group: Cg*s = %d bytes is too many "
+                    "for this alignment", Cg * s);
+    const int64_t C = (int64_t)G * Cg, npix = (int64_t)N * p.Ho * p.Wo;
+    const int64_t xb = (int64_t)N * H * W * C * s, ob = npix * C * s;
+    const int64_t offb = ((npix - 1) * p.off_row + (int64_t)G * 2 * p.P) * s;
+    const int64_t mb = ((npix - 1) * p.mask_row + (int64_t)G * p.P) * s;
+    const int64_t gxb = (int64_t)N * H * W * C * 4;
+    const int64_t goffb = ((npix - 1) * p.off_row + (int64_t)G * 2 * p.P) * 4;
+    const int64_t gmb = ((npix - 1) * p.mask_row + (int64_t)G * p.P) * 4;
+    struct Span { const void* p; int64_t b; };
+    const Span in[4] = {{x, xb}, {offset, offb}, {mask, mb}, {grad_out, ob}};
+    const Span outs[3] = {{grad_x, gxb}, {grad_offset, goffb}, {grad_mask, gmb}};
+    for (const Span& o : outs) {
+        if (!o.p) continue;
+        for (const Span& i : in)
+            if (overlaps(o.p, o.b, i.p, i.b)) return fail(DCNV4_ERR_ALIAS, "a gradient overlaps an input");
+    }
+    if (grad_x && ((grad_offset && overlaps(grad_x, gxb, grad_offset, goffb)) ||
+                   (grad_mask && overlaps(grad_x, gxb, grad_mask, gmb))))
+        return fail(DCNV4_ERR_ALIAS, "grad_x overlaps grad_offset or grad_mask");
+    if (!grad_x && !grad_offset && !grad_mask) return DCNV4_OK;
+    st = check_device();
+    if (st != DCNV4_OK) return st;
+    const hipError_t e = dcnv4::launch_backward(p, grad_out, grad_x, grad_offset, grad_mask, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DCNV4_ERR_HIP, "launch of the backward failed: %s", hipGetErrorString(e));
+    return DCNV4_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int dcnv4_backward(const void* x, const void* offset, const void* mask, const void* grad_out,
+                   float* grad_x, float* grad_offset, float* grad_mask,
+                   int N, int H, int W, int G, int Cg,
+                   int K, int stride, int pad, int dilation, float offset_scale,
+                   int remove_center, int64_t offset_row, int64_t mask_row,
+                   int dtype, void* stream)
+{
+    return backward_impl(x, offset, mask, grad_out, grad_x, grad_offset, grad_mask, N, H, W, G, Cg, K, stride,
+                         pad, dilation, offset_scale, remove_center, offset_row, mask_row, dtype, stream);
+}
 
 int dcnv4_forward(const void* x, const void* offset, const void* mask, void* out,
                   int N, int H, int W, int G, int Cg,

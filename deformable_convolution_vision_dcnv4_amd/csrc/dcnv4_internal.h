@@ -49,4 +49,11 @@ void make_plan(const Problem& p, Plan* plan);
 // Enqueue the kernel chosen by make_plan on `stream`.
 hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream);
 
+// Backward: bytes per lane per vector for these pointers (lanes per unit =
+// Cg*s / that), and the launch (zero grad_x, then the gradient kernel).
+// Null gradient pointers are skipped.
+int backward_vec_bytes(const Problem& p, const void* gout);
+hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
+                           hipStream_t stream);
+
 }  // namespace dcnv4

@@ -70,6 +70,30 @@ struct KArgs {
     uint32_t lds_bytes;             // all dynamic LDS
 };
 
+// Backward kernel arguments (elements of the I/O type unless named *_bytes;
+// the gradients are binary32 with the inputs' element strides).
+struct BArgs {
+    const void* x;
+    const void* off;
+    const void* msk;
+    const void* gout;
+    float* gx;
+    float* goff;
+    float* gmask;
+    int H, W, G, Cg, C, K, P, stride, pad, dil, Ho, Wo;
+    int remove_center;
+    int64_t off_row, mask_row;
+    int64_t img_x_elems, img_out_elems, img_off_elems, img_mask_elems;
+    uint32_t img_x_bytes;
+    float offset_scale;
+    int vec_bytes;                  // bytes per lane per vector
+    int lanes;                      // lanes per unit (<= 64)
+    int units_per_wave;
+    uint32_t units_img;
+    int64_t units_total;
+    FastDiv div_units_img, div_G, div_Wo;
+};
+
 hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hipStream_t stream);
 hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);
 

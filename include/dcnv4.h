@@ -112,6 +112,36 @@ int dcnv4_forward_ex(const void* x, const void* offset, const void* mask, void* 
                      int remove_center, int64_t offset_row, int64_t mask_row,
                      int dtype, void* stream);
 
+/*
+ * Gradients of the operator (dcnv4_forward_ex's arguments) given grad_out =
+ * dL/dout [N, Ho, Wo, G*Cg] in the I/O type.  The forward is
+ *   out = sum_k m_k * sum_q tri(py_k - qy) tri(px_k - qx) x[q],
+ *   tri(t) = max(0, 1 - |t|),  p_k = base_k + offset_scale * offset_k,
+ * (the definition of jsqmd.com/news/933833 section 1 in triangle-kernel form);
+ * its derivative with respect to a position is taken from the right at
+ * integer coordinates (the side whose corners floor(p), floor(p)+1 the
+ * forward uses), and points the forward skips have zero gradient.
+ * Gradients are binary32, whatever the I/O type:
+ *   grad_x       [N, H, W, G*Cg], overwritten (zeroed, then accumulated)
+ *   grad_offset  rows of offset_row elements per output pixel, like offset;
+ *                only the G*2*P gradient elements of each row are written
+ *   grad_mask    rows of mask_row elements, like mask; G*P elements written
+ * Any gradient pointer may be NULL (not computed).  Arithmetic is binary32;
+ * grad_offset and grad_mask are summed in a fixed order (reproducible);
+ * grad_x is accumulated with hardware atomic adds, whose order is not fixed
+ * (results may differ in the last bits between runs).  Gradients must not
+ * overlap the inputs or grad_x; grad_offset and grad_mask may interleave
+ * (one packed tensor) but must not share elements.  Needs Cg*s <= 64 vectors
+ * of the widest width the pointers allow (else DCNV4_ERR_TOO_LARGE).
+ * Validation, ownership and stream semantics as for dcnv4_forward.
+ */
+int dcnv4_backward(const void* x, const void* offset, const void* mask, const void* grad_out,
+                   float* grad_x, float* grad_offset, float* grad_mask,
+                   int N, int H, int W, int G, int Cg,
+                   int K, int stride, int pad, int dilation, float offset_scale,
+                   int remove_center, int64_t offset_row, int64_t mask_row,
+                   int dtype, void* stream);
+
 /* Ho or Wo for an input extent; <= 0 when the arguments admit no output. */
 int dcnv4_output_dim(int in, int K, int stride, int pad, int dilation);
 

@@ -65,7 +65,11 @@
  *       (an integer coordinate, where the bilinear corners change): the
  *       derivative from the right, which is the one that belongs to the
  *       corners floor(p) and floor(p)+1 that the forward uses.  Points the
- *       forward skips have zero gradient.
+ *       forward skips have zero gradient.  With f32_positions the sampling
+ *       positions are the forward's binary32 ones (one fmaf, as in the
+ *       sequence above) and everything after them is double: the reference
+ *       for a binary32 evaluation of the gradients, whose positions carry
+ *       that rounding by construction.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
@@ -400,7 +404,8 @@ int dcnv4_oracle_backward_f64(const double* x, const double* offset, const doubl
                               double* grad_mask, double* abs_x, double* cnt_x, double* abs_offset,
                               double* abs_mask, int N, int H, int W, int G, int Cg, int K,
                               int stride, int pad, int dil, double offset_scale,
-                              int remove_center, int64_t off_stride, int64_t mask_stride)
+                              int remove_center, int64_t off_stride, int64_t mask_stride,
+                              int f32_positions)
 {
     shape_t s;
     if (make_shape(&s, N, H, W, G, Cg, K, stride, pad, dil, remove_center,
@@ -428,8 +433,12 @@ int dcnv4_oracle_backward_f64(const double* x, const double* offset, const doubl
                 const double dx = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + k];
                 const double dy = offset[pix * s.off_stride + (int64_t)g * 2 * s.P + s.P + k];
                 const double m = mask[pix * s.mask_stride + (int64_t)g * s.P + k];
-                const double px = (double)(wo * stride - pad + j * dil) + offset_scale * dx;
-                const double py = (double)(ho * stride - pad + i * dil) + offset_scale * dy;
+                double px = (double)(wo * stride - pad + j * dil) + offset_scale * dx;
+                double py = (double)(ho * stride - pad + i * dil) + offset_scale * dy;
+                if (f32_positions) {
+                    px = (double)fmaf((float)dx, (float)offset_scale, (float)(wo * stride - pad + j * dil));
+                    py = (double)fmaf((float)dy, (float)offset_scale, (float)(ho * stride - pad + i * dil));
+                }
                 double d_px = 0.0, d_py = 0.0, d_m = 0.0, a_px = 0.0, a_py = 0.0, a_m = 0.0;
                 if (px > -1.0 && px < W && py > -1.0 && py < H) {
                     const int x0 = (int)floor(px), y0 = (int)floor(py);

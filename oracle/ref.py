@@ -44,7 +44,7 @@ def lib():
         L.dcnv4_oracle_forward_f32.restype = i32
         L.dcnv4_oracle_forward_f64.argtypes = [vp, vp, vp, vp] + [i32] * 9 + [f64, i32, i64, i64]
         L.dcnv4_oracle_forward_f64.restype = i32
-        L.dcnv4_oracle_backward_f64.argtypes = [vp] * 11 + [i32] * 9 + [f64, i32, i64, i64]
+        L.dcnv4_oracle_backward_f64.argtypes = [vp] * 11 + [i32] * 9 + [f64, i32, i64, i64, i32]
         L.dcnv4_oracle_backward_f64.restype = i32
         for name in ("f16_to_f32_array", "bf16_to_f32_array", "f32_to_f16_array", "f32_to_bf16_array"):
             fn = getattr(L, "dcnv4_oracle_" + name)
@@ -132,13 +132,15 @@ def forward_f64(x, offset, mask, *, K=3, stride=1, pad=1, dil=1, offset_scale=1.
 
 
 def backward_f64(x, offset, mask, grad_out, *, K=3, stride=1, pad=1, dil=1, offset_scale=1.0,
-                 remove_center=False, groups=None, bounds=False):
+                 remove_center=False, groups=None, bounds=False, f32_positions=False):
     """Gradients of the plain definition in double precision (inputs float64).
 
     Returns (grad_x [N,H,W,C], grad_offset [N,Ho,Wo,G*2*P], grad_mask
     [N,Ho,Wo,G*P]).  With ``bounds``, also a dict of the absolute-value sums
     and term counts that bound a binary32 evaluation's rounding error:
-    {"abs_x", "cnt_x", "abs_offset", "abs_mask"} (same shapes)."""
+    {"abs_x", "cnt_x", "abs_offset", "abs_mask"} (same shapes).  With
+    ``f32_positions`` the sampling positions are the forward's binary32 ones
+    (the reference for a binary32 evaluation)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     grad_out = np.ascontiguousarray(grad_out, dtype=np.float64)
     if offset.dtype != np.float64 or mask.dtype != np.float64:
@@ -156,7 +158,8 @@ def backward_f64(x, offset, mask, grad_out, *, K=3, stride=1, pad=1, dil=1, offs
     ptrs = [_ptr(e) for e in extra] if bounds else [null] * 4
     rc = lib().dcnv4_oracle_backward_f64(_ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out), _ptr(gx),
                                          _ptr(goff), _ptr(gm), *ptrs, N, H, W, G, Cg, K, stride, pad, dil,
-                                         float(offset_scale), int(bool(remove_center)), G * 2 * P, G * P)
+                                         float(offset_scale), int(bool(remove_center)), G * 2 * P, G * P,
+                                         int(bool(f32_positions)))
     if rc != 0:
         raise RuntimeError(f"oracle backward failed with status {rc}")
     if bounds:

@@ -124,3 +124,35 @@ def test_plan_full_window_for_small_images():
     assert st == OK and pl.full_window == 1
     assert (pl.window_h, pl.window_w) == (16, 16)
     assert pl.grid * pl.groups_per_block == 64 * 16
+
+
+GX, GOFF, GMSK, GOUT = 0x50000000, 0x60000000, 0x70000000, 0x80000000
+
+
+def bcall(**kw):
+    a = dict(x=X, off=OFF, msk=MSK, gout=GOUT, gx=GX, goff=GOFF, gm=GMSK, N=2, H=8, W=8, G=4, Cg=16, K=3,
+             s=1, p=1, d=1, scale=1.0, rc=0, orow=0, mrow=0, dtype=1)
+    a.update(kw)
+    return binding.lib().dcnv4_backward(a["x"], a["off"], a["msk"], a["gout"], a["gx"], a["goff"], a["gm"],
+                                        a["N"], a["H"], a["W"], a["G"], a["Cg"], a["K"], a["s"], a["p"],
+                                        a["d"], a["scale"], a["rc"], a["orow"], a["mrow"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), ERR_DTYPE), (dict(G=0), ERR_SHAPE), (dict(K=0), ERR_PARAM),
+    (dict(scale=float("nan")), ERR_PARAM), (dict(rc=1, K=2), ERR_PARAM),
+    (dict(x=0), ERR_NULL), (dict(gout=0), ERR_NULL), (dict(off=0), ERR_NULL),
+    (dict(gx=GX + 2), ERR_ALIGN), (dict(goff=GOFF + 1), ERR_ALIGN), (dict(gout=GOUT + 1), ERR_ALIGN),
+    (dict(gx=X), ERR_ALIAS), (dict(goff=GOUT + 64), ERR_ALIAS), (dict(gm=MSK), ERR_ALIAS),
+    (dict(gx=GOFF - 64), ERR_ALIAS),
+    (dict(Cg=1024, dtype=0), ERR_TOO_LARGE),
+    (dict(orow=10), ERR_PARAM),
+])
+def test_backward_rejects_invalid_arguments(kw, status):
+    assert bcall(**kw) == status
+    assert binding.last_error() != ""
+
+
+def test_backward_empty_batch_and_no_gradients_are_noops():
+    assert bcall(N=0, x=0, off=0, msk=0, gout=0, gx=0, goff=0, gm=0) == OK
+    assert bcall(gx=0, goff=0, gm=0) == OK

@@ -1,0 +1,126 @@
+"""GPU parity of the backward (dcnv4_backward through the C ABI) with the
+oracle's gradients.
+
+Reference: the oracle's double-precision gradients at the forward's binary32
+sampling positions, on the exact binary32 values of the I/O-typed inputs.
+The GPU evaluates them in binary32; with u = 2^-24, each gradient element is
+a sum of n products of a few rounded factors, so its error is bounded by
+(n + c) * u * (sum of the terms' absolute values), first order, in any
+summation order.  The oracle returns those absolute sums and term counts:
+  grad_x       n = number of scattered terms (order not fixed: atomics), c = 6
+  grad_mask    n = 4*Cg products per point, c = 8
+  grad_offset  n = 4*Cg products of differences per point, c = 10
+"""
+import numpy as np
+import pytest
+import torch
+
+from deformable_convolution_vision_dcnv4_amd import binding
+from deformable_convolution_vision_dcnv4_amd import inputs as gen
+from deformable_convolution_vision_dcnv4_amd.workloads import WORKLOADS, Workload
+from oracle import ref
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    binding.lib()
+    yield
+
+
+def f64(a, dtype):
+    return ref.to_f32(a, dtype).astype(np.float64)
+
+
+def grad_out_for(wl, dtype, seed):
+    Ho, Wo = wl.out_hw()
+    w2 = Workload("gout", wl.N, Ho, Wo, wl.G, wl.Cg, (dtype,), seed=seed)
+    g, _, _ = gen.make_inputs(w2, dtype)
+    return g
+
+
+def check(wl, dtype, seed=41, packed=False):
+    x, off, m = gen.make_inputs(wl, dtype)
+    go = grad_out_for(wl, dtype, seed)
+    kw = dict(K=wl.K, stride=wl.stride, pad=wl.pad, dil=wl.dil, offset_scale=wl.offset_scale,
+              remove_center=wl.remove_center)
+    rx, roff, rm, rgo = f64(x, dtype), f64(off, dtype), f64(m, dtype), f64(go, dtype)
+    gx_ref, goff_ref, gm_ref, b = ref.backward_f64(rx, roff, rm, rgo, bounds=True, f32_positions=True, **kw)
+    G, P = wl.G, wl.P
+    xd, god = gu.dev(x, dtype), gu.dev(go, dtype)
+    if packed:
+        pk = gu.dev(np.ascontiguousarray(np.concatenate([off, m], -1)), dtype)
+        od, md = pk[..., :2 * G * P], pk[..., 2 * G * P:]
+    else:
+        od, md = gu.dev(off, dtype), gu.dev(m, dtype)
+    gu.announce(f"backward {wl.describe(dtype)} remove_center={wl.remove_center} packed={packed}")
+    gx, goff, gm = binding.backward(xd, od, md, god, kernel_size=wl.K, stride=wl.stride, pad=wl.pad,
+                                    dilation=wl.dil, offset_scale=wl.offset_scale,
+                                    remove_center=wl.remove_center, group=G)
+    torch.cuda.synchronize()
+    gx, goff, gm = (t.cpu().numpy().astype(np.float64) for t in (gx, goff, gm))
+    tol_x = (b["cnt_x"] + 6) * U * b["abs_x"] + 1e-300
+    tol_m = (4 * wl.Cg + 8) * U * b["abs_mask"] + 1e-300
+    tol_o = (4 * wl.Cg + 10) * U * b["abs_offset"] + 1e-300
+    ex, em, eo = np.abs(gx - gx_ref), np.abs(gm - gm_ref), np.abs(goff - goff_ref)
+    print(f"  max err x {ex.max():.3g} (tol {tol_x.max():.3g}), mask {em.max():.3g}, offset {eo.max():.3g}")
+    assert np.all(ex <= tol_x), f"grad_x: {np.sum(ex > tol_x)} elements beyond the bound"
+    assert np.all(em <= tol_m), f"grad_mask: {np.sum(em > tol_m)} elements beyond the bound"
+    assert np.all(eo <= tol_o), f"grad_offset: {np.sum(eo > tol_o)} elements beyond the bound"
+    return gx, goff, gm
+
+
+CASES = []
+for dtype in ("f32", "f16", "bf16"):
+    for Cg in (16, 6, 40):
+        CASES.append((Workload("bwd", 2, 11, 13, 3, Cg, (dtype,), offset_dist=("normal", 2.0),
+                               mask_dist=("normal", 0.7), seed=43), dtype))
+for K, s, p, d, rc in ((5, 1, 2, 1, False), (3, 2, 1, 1, False), (3, 1, 2, 2, False), (3, 1, 1, 1, True),
+                       (1, 1, 0, 1, False)):
+    CASES.append((Workload("bwd_geom", 2, 12, 10, 2, 8, ("f32",), offset_dist=("normal", 1.5), K=K, stride=s,
+                           pad=p, dil=d, remove_center=rc, offset_scale=0.75, seed=44), "f32"))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[1]}-Cg{c[0].Cg}-K{c[0].K}s{c[0].stride}d{c[0].dil}"
+                                                      f"{'-rc' if c[0].remove_center else ''}")
+def test_backward_matches_oracle(case):
+    wl, dtype = case
+    check(wl, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_packed_rows(dtype):
+    wl = Workload("bwd_packed", 2, 9, 10, 4, 16, (dtype,), offset_dist=("normal", 2.0), remove_center=True, seed=45)
+    check(wl, dtype, packed=True)
+
+
+@pytest.mark.parametrize("name,dtype", [("fiit_stage3", "f16"), ("tiny", "f32")])
+def test_backward_workloads(name, dtype):
+    check(WORKLOADS[name], dtype)
+
+
+def test_backward_offset_and_mask_gradients_are_reproducible():
+    wl = Workload("bwd_rep", 2, 16, 16, 4, 16, ("f16",), offset_dist=("normal", 2.0), seed=46)
+    x, off, m = gen.make_inputs(wl, "f16")
+    go = grad_out_for(wl, "f16", 47)
+    args = [gu.dev(a, "f16") for a in (x, off, m, go)]
+    r1 = binding.backward(*args)
+    r2 = binding.backward(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
+    assert torch.allclose(r1[0], r2[0], rtol=1e-5, atol=1e-6)
+
+
+def test_backward_points_outside_have_zero_gradient():
+    wl = Workload("bwd_oob", 2, 6, 7, 2, 8, ("f32",), seed=48)
+    x, off, m = gen.make_inputs(wl, "f32")
+    go = grad_out_for(wl, "f32", 49)
+    for fill in (100.0, -100.0, float("nan")):
+        o = np.full_like(off, fill)
+        gx, goff, gm = binding.backward(gu.dev(x, "f32"), gu.dev(o, "f32"), gu.dev(m, "f32"), gu.dev(go, "f32"))
+        torch.cuda.synchronize()
+        assert not torch.any(gx) and not torch.any(goff) and not torch.any(gm), fill

@@ -151,3 +151,21 @@ def test_bounds_dominate_the_gradients():
     assert np.all(np.abs(gm) <= b["abs_mask"] * (1 + 1e-12))
     assert np.all(np.abs(goff) <= 2 * b["abs_offset"] * (1 + 1e-12))
     assert np.array_equal(b["cnt_x"], np.round(b["cnt_x"])) and b["cnt_x"].max() >= 1
+
+
+def test_f32_positions_equal_exact_positions_for_dyadic_offsets():
+    """Offsets that are multiples of 1/64 (and scale 0.5) give positions that
+    binary32 represents exactly: both position modes agree exactly; with
+    general offsets they differ only through the rounding of the positions."""
+    rng = np.random.default_rng(38)
+    x, off, m, go, kw = case(rng)
+    dy = np.round(off * 64) / 64
+    a = ref.backward_f64(x, dy, m, go, offset_scale=0.5, **kw)
+    b = ref.backward_f64(x, dy, m, go, offset_scale=0.5, f32_positions=True, **kw)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    c = ref.backward_f64(x, off, m, go, offset_scale=0.3, **kw)
+    d = ref.backward_f64(x, off, m, go, offset_scale=0.3, f32_positions=True, **kw)
+    assert not all(np.array_equal(u, v) for u, v in zip(c, d))
+    for u, v in zip(c, d):
+        np.testing.assert_allclose(u, v, rtol=1e-4, atol=1e-4)
