@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="fiit_stage1")
+    ap.add_argument("--op", default="forward", choices=("forward", "backward"),
+                    help="forward (the headline) or the backward (gradients of x, offsets, weights)")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's last)")
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotating input copies")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
@@ -139,11 +141,25 @@ def main():
     argv = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr(), wl.N, wl.H, wl.W,
              wl.G, wl.Cg, wl.K, wl.stride, wl.pad, wl.dil, wl.offset_scale, dcode, sptr) for s in sets]
     fwd = L.dcnv4_forward
+    if args.op == "backward":
+        # grad_out: a copy of the output-shaped buffer filled with the forward's result;
+        # gradients in binary32, one set shared by all steps (each step overwrites them)
+        Pn = wl.P
+        gx = torch.empty((wl.N, wl.H, wl.W, wl.C), dtype=torch.float32, device=dev)
+        goff = torch.empty((wl.N, Ho, Wo, wl.G * 2 * Pn), dtype=torch.float32, device=dev)
+        gm = torch.empty((wl.N, Ho, Wo, wl.G * Pn), dtype=torch.float32, device=dev)
+        for a in argv:
+            assert fwd(*a) == 0
+        torch.cuda.synchronize()
+        bargv = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr(), gx.data_ptr(),
+                  goff.data_ptr(), gm.data_ptr(), wl.N, wl.H, wl.W, wl.G, wl.Cg, wl.K, wl.stride, wl.pad,
+                  wl.dil, wl.offset_scale, int(wl.remove_center), 0, 0, dcode, sptr) for s in sets]
+        bwd = L.dcnv4_backward
 
     def step(i):
-        st = fwd(*argv[i % copies])
+        st = bwd(*bargv[i % copies]) if args.op == "backward" else fwd(*argv[i % copies])
         if st != 0:
-            raise RuntimeError(f"dcnv4_forward failed: {binding.status_string(st)}: {binding.last_error()}")
+            raise RuntimeError(f"dcnv4 {args.op} failed: {binding.status_string(st)}: {binding.last_error()}")
 
     plan = binding.query_plan(sets[0][0], sets[0][1], sets[0][2], sets[0][3], kernel_size=wl.K,
                               stride=wl.stride, pad=wl.pad, dilation=wl.dil, offset_scale=wl.offset_scale)
@@ -182,19 +198,20 @@ def main():
     log(f"per-launch event pairs: median {np.median(durs) * 1e3:.2f} us, "
         f"p10 {np.percentile(durs, 10) * 1e3:.2f} us, p90 {np.percentile(durs, 90) * 1e3:.2f} us")
 
-    alg_bytes = wl.algorithmic_bytes(dtype)
+    alg_bytes = wl.algorithmic_bytes(dtype) if args.op == "forward" else wl.backward_bytes(dtype)
     ms_per_step = wall * 1e3 / args.steps
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, dtype, alg_bytes)
+    traffic = load_traffic(wl.name if args.op == "forward" else wl.name + "_backward", dtype, alg_bytes)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "forward":
         log("timing the CPU oracle baseline")
         cpu = cpu_baseline(wl, dtype, x, off, m, args.cpu_budget)
 
     rec = {
-        "metric": "DCNv4 fwd GB/s + Gsamples/s per MI355X; % of HBM roofline",
+        "metric": ("DCNv4 fwd GB/s + Gsamples/s per MI355X; % of HBM roofline" if args.op == "forward" else
+                   "DCNv4 bwd GB/s + Gsamples/s per MI355X; % of HBM roofline"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -208,6 +225,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; no dataset, no trained weights)",
         "config": {
             "workload": wl.describe(dtype),
+            "op": args.op,
             "N": wl.N, "H": wl.H, "W": wl.W, "G": wl.G, "Cg": wl.Cg, "K": wl.K,
             "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil, "offset_scale": wl.offset_scale,
             "inputs": {"x": list(wl.x_dist), "offset": list(wl.offset_dist), "mask": list(wl.mask_dist),

@@ -25,6 +25,8 @@
 
 #include <string.h>
 
+#include <numeric>
+
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
 #include "dcnv4_kernels.h"
@@ -80,7 +82,7 @@ __device__ __forceinline__ float unit_sum(float v, int L, int lane0)
     return s;
 }
 
-template <int DT, int VB>
+template <int DT, int VB, int KT>
 __global__ void __launch_bounds__(256) k_backward(BArgs a)
 {
     using E = Elem<DT>;
@@ -129,10 +131,12 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a)
     const float fW = (float)a.W, fH = (float)a.H;
     const int bx0 = (int)wo * a.stride - a.pad;
     const int by0 = (int)ho * a.stride - a.pad;
-    const int K = a.K, KK = K * K, center = KK / 2;
-    int k = 0;
-    for (int q = 0; q < KK; ++q) {
+    const int K = KT > 0 ? KT : a.K, KK = K * K, center = KK / 2;
+    constexpr int kUnroll = KT > 0 ? KT * KT : 1;
+#pragma unroll kUnroll
+    for (int q = 0; q < (KT > 0 ? KT * KT : KK); ++q) {
         if (a.remove_center && q == center) continue;
+        const int k = (a.remove_center && q > center) ? q - 1 : q;
         const int i = q / K, j = q - (q / K) * K;
         const float dx = E::to_f(os[k]), dy = E::to_f(os[a.P + k]), m = E::to_f(ms[k]);
         float px = fmaf(dx, a.offset_scale, (float)(bx0 + j * a.dil));
@@ -197,20 +201,136 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a)
             }
             if (a.gmask) a.gmask[mrow + k] = valid ? tm : 0.0f;
         }
-        ++k;
     }
+}
+
+// x's gradient of one (image, group, chunk of CC channels), accumulated in an
+// LDS copy of the zero-bordered image [-1, H] x [-1, W] (binary32, one plane
+// per channel, so that lanes on neighbouring pixels add to different banks):
+// every corner of every valid point lands inside it, corners off the image
+// land on the border, which is dropped.  The workgroup owns that
+// slice of grad_x, so it is written once with plain stores: no global
+// atomics and no separate zeroing.  LDS adds from different lanes to one
+// pixel happen in no fixed order.
+template <int DT, int RC, int CC>
+__global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
+{
+    using E = Elem<DT>;
+    constexpr int s = E::kBytes;
+    constexpr int P = 9 - RC;                 // K = 3
+    extern __shared__ float acc[];
+    const int chunks = a.Cg / CC;
+    const uint32_t b = blockIdx.x;
+    const uint32_t n = b / (uint32_t)(a.G * chunks);
+    const uint32_t r = b - n * (uint32_t)(a.G * chunks);
+    const uint32_t g = r / (uint32_t)chunks, ch = r - g * (uint32_t)chunks;
+    const int WP = a.W + 2;                                  // bordered row
+    const int plane = (a.H + 2) * WP;
+    for (int i = threadIdx.x; i < plane * CC; i += blockDim.x) acc[i] = 0.0f;
+    __syncthreads();
+
+    const char* oimg = static_cast<const char*>(a.off) + (int64_t)n * a.img_off_elems * s;
+    const char* mimg = static_cast<const char*>(a.msk) + (int64_t)n * a.img_mask_elems * s;
+    const char* gimg = static_cast<const char*>(a.gout) + (int64_t)n * a.img_out_elems * s;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(oimg, a.img_off_bytes);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mimg, a.img_mask_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gimg, a.img_out_bytes);
+    const float fW = (float)a.W, fH = (float)a.H;
+    const int npix = a.Ho * a.Wo;
+    // lanes of a wave take pixels `spread` apart (spread coprime with npix, so
+    // t -> t * spread mod npix visits every pixel once): their corners rarely
+    // coincide, and coinciding LDS atomic adds in one instruction serialise
+    const uint32_t spread = (uint32_t)a.spread;
+    for (int t = threadIdx.x; t < npix; t += blockDim.x) {
+        const int pix = (int)(((uint64_t)t * spread) % (uint32_t)npix);
+        const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
+        // the unit's offset, weight and output-gradient rows: all loads in flight together
+        RowLoad<DT, 2 * P> orow;
+        RowLoad<DT, P> mrow;
+        RowLoad<DT, CC> grow;
+        orow.load(ro, (uint32_t)(((int64_t)pix * a.off_row + (int64_t)g * 2 * P) * s));
+        mrow.load(rm, (uint32_t)(((int64_t)pix * a.mask_row + (int64_t)g * P) * s));
+        grow.load(rg, (uint32_t)(((int64_t)pix * a.C + (int64_t)g * a.Cg + (int64_t)ch * CC) * s));
+        float gr[CC];
+#pragma unroll
+        for (int c = 0; c < CC; ++c) gr[c] = grow.get(c);
+        const int bx0 = wo * a.stride - a.pad, by0 = ho * a.stride - a.pad;
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int q = (RC && k >= 4) ? k + 1 : k;
+            const int i = q / 3, j = q % 3;
+            const float px = fmaf(orow.get(k), a.offset_scale, (float)(bx0 + j * a.dil));
+            const float py = fmaf(orow.get(P + k), a.offset_scale, (float)(by0 + i * a.dil));
+            const float m = mrow.get(k);
+            if (!((px > -1.0f) & (px < fW) & (py > -1.0f) & (py < fH))) continue;
+            const float fx = floorf(px), fy = floorf(py);
+            const int x0 = (int)fx, y0 = (int)fy;
+            const float lx = px - fx, ly = py - fy;
+            const float hx = 1.0f - lx, hy = 1.0f - ly;
+            const float mhy = m * hy, mly = m * ly;
+            const float w00 = mhy * hx, w01 = mhy * lx, w10 = mly * hx, w11 = mly * lx;
+            // corner (y0, x0) of the bordered image; the others follow
+            float* c00 = acc + (y0 + 1) * WP + (x0 + 1);
+#pragma unroll
+            for (int c = 0; c < CC; ++c) {
+                float* pc = c00 + c * plane;
+                atomicAdd(pc, w00 * gr[c]);
+                atomicAdd(pc + 1, w01 * gr[c]);
+                atomicAdd(pc + WP, w10 * gr[c]);
+                atomicAdd(pc + WP + 1, w11 * gr[c]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // the image's interior to grad_x[n, y, x, g*Cg + ch*CC + c]
+    float* gx = a.gx + (int64_t)n * a.img_x_elems + g * a.Cg + ch * CC;
+    const int interior = a.H * a.W * CC;
+    for (int i = threadIdx.x; i < interior; i += blockDim.x) {
+        const int c = i % CC, p = i / CC;
+        const int y = p / a.W, x = p - (p / a.W) * a.W;
+        gx[(int64_t)p * a.C + c] = acc[c * plane + (y + 1) * WP + (x + 1)];
+    }
+}
+
+template <int DT, int RC>
+void launch_bx_cc(const BArgs& a, unsigned grid, size_t lds, hipStream_t stream)
+{
+    switch (a.cc) {
+        case 16: hipLaunchKernelGGL((k_backward_x<DT, RC, 16>), dim3(grid), dim3(1024), lds, stream, a); break;
+        case 8: hipLaunchKernelGGL((k_backward_x<DT, RC, 8>), dim3(grid), dim3(1024), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((k_backward_x<DT, RC, 4>), dim3(grid), dim3(1024), lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((k_backward_x<DT, RC, 2>), dim3(grid), dim3(1024), lds, stream, a); break;
+        default: hipLaunchKernelGGL((k_backward_x<DT, RC, 1>), dim3(grid), dim3(1024), lds, stream, a); break;
+    }
+}
+
+template <int DT>
+void launch_bx(const BArgs& a, unsigned grid, size_t lds, hipStream_t stream)
+{
+    if (a.remove_center) launch_bx_cc<DT, 1>(a, grid, lds, stream);
+    else launch_bx_cc<DT, 0>(a, grid, lds, stream);
+}
+
+template <int DT, int VB>
+void launch_vb(const BArgs& a, int64_t grid, hipStream_t stream)
+{
+    if (a.K == 3)
+        hipLaunchKernelGGL((k_backward<DT, VB, 3>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_backward<DT, VB, 0>), dim3((unsigned)grid), dim3(256), 0, stream, a);
 }
 
 template <int DT>
 hipError_t launch_dt(const BArgs& a, int64_t grid, hipStream_t stream)
 {
     switch (a.vec_bytes) {
-        case 16: hipLaunchKernelGGL((k_backward<DT, 16>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((k_backward<DT, 8>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((k_backward<DT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+        case 16: launch_vb<DT, 16>(a, grid, stream); break;
+        case 8: launch_vb<DT, 8>(a, grid, stream); break;
+        case 4: launch_vb<DT, 4>(a, grid, stream); break;
         case 2:
             if constexpr (DT != DCNV4_F32) {
-                hipLaunchKernelGGL((k_backward<DT, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+                launch_vb<DT, 2>(a, grid, stream);
                 break;
             }
             return hipErrorInvalidValue;
@@ -252,6 +372,9 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     a.img_off_elems = (int64_t)p.Ho * p.Wo * p.off_row;
     a.img_mask_elems = (int64_t)p.Ho * p.Wo * p.mask_row;
     a.img_x_bytes = (uint32_t)(a.img_x_elems * s);
+    a.img_out_bytes = (uint32_t)(a.img_out_elems * s);
+    a.img_off_bytes = (uint32_t)(((((int64_t)p.Ho * p.Wo - 1) * p.off_row + (int64_t)p.G * 2 * p.P) * s + 3) & ~3ll);
+    a.img_mask_bytes = (uint32_t)(((((int64_t)p.Ho * p.Wo - 1) * p.mask_row + (int64_t)p.G * p.P) * s + 3) & ~3ll);
     a.vec_bytes = backward_vec_bytes(p, gout);
     a.lanes = p.Cg * s / a.vec_bytes;
     a.units_per_wave = 64 / a.lanes;
@@ -261,20 +384,56 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     a.div_G = make_fastdiv((uint32_t)p.G);
     a.div_Wo = make_fastdiv((uint32_t)p.Wo);
 
-    if (gx) {
+    // x's gradient in LDS when a channel chunk of the bordered image fits
+    a.cc = gx ? backward_x_chunk(p) : 0;
+    if (gx && !a.cc) {
         const int64_t n = (int64_t)p.N * a.img_x_elems;
         const int64_t blocks = ceil_div(ceil_div(n, 4), 256);
         hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, gx, n);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t grid = ceil_div(a.units_total, 4 * (int64_t)a.units_per_wave);
-    switch (p.dtype) {
-        case DCNV4_F32: return launch_dt<DCNV4_F32>(a, grid, stream);
-        case DCNV4_F16: return launch_dt<DCNV4_F16>(a, grid, stream);
-        case DCNV4_BF16: return launch_dt<DCNV4_BF16>(a, grid, stream);
-        default: return hipErrorInvalidValue;
+    if (goff || gmask || (gx && !a.cc)) {
+        BArgs b = a;
+        if (a.cc) b.gx = nullptr;          // the LDS kernel below takes x's gradient
+        const int64_t grid = ceil_div(a.units_total, 4 * (int64_t)a.units_per_wave);
+        hipError_t e = hipErrorInvalidValue;
+        switch (p.dtype) {
+            case DCNV4_F32: e = launch_dt<DCNV4_F32>(b, grid, stream); break;
+            case DCNV4_F16: e = launch_dt<DCNV4_F16>(b, grid, stream); break;
+            case DCNV4_BF16: e = launch_dt<DCNV4_BF16>(b, grid, stream); break;
+            default: break;
+        }
+        if (e != hipSuccess) return e;
     }
+    if (a.cc) {
+        // the smallest stride >= 13 coprime with the pixel count
+        const int64_t npix = (int64_t)p.Ho * p.Wo;
+        int sp = 13;
+        while (std::gcd((int64_t)sp, npix) != 1) ++sp;
+        a.spread = npix > 1 ? sp : 1;
+        const unsigned grid = (unsigned)((int64_t)p.N * p.G * (p.Cg / a.cc));
+        const size_t lds = (size_t)(p.H + 2) * (p.W + 2) * a.cc * 4;
+        switch (p.dtype) {
+            case DCNV4_F32: launch_bx<DCNV4_F32>(a, grid, lds, stream); break;
+            case DCNV4_F16: launch_bx<DCNV4_F16>(a, grid, lds, stream); break;
+            case DCNV4_BF16: launch_bx<DCNV4_BF16>(a, grid, lds, stream); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+int backward_x_chunk(const Problem& p)
+{
+    // K = 3: the most channels (a power of two dividing Cg, at most 16) whose
+    // bordered image fits in LDS
+    if (p.K != 3) return 0;
+    const int64_t cell = (int64_t)(p.H + 2) * (p.W + 2) * 4;
+    for (int cc = 16; cc >= 1; cc /= 2)
+        if (p.Cg % cc == 0 && cell * cc <= kLdsPerCu) return cc;
+    return 0;
 }
 
 }  // namespace dcnv4

@@ -53,6 +53,8 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
 // Cg*s / that), and the launch (zero grad_x, then the gradient kernel).
 // Null gradient pointers are skipped.
 int backward_vec_bytes(const Problem& p, const void* gout);
+// Channels per workgroup of the LDS x-gradient kernel (0: global atomics instead).
+int backward_x_chunk(const Problem& p);
 hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
                            hipStream_t stream);
 

@@ -84,11 +84,13 @@ struct BArgs {
     int remove_center;
     int64_t off_row, mask_row;
     int64_t img_x_elems, img_out_elems, img_off_elems, img_mask_elems;
-    uint32_t img_x_bytes;
+    uint32_t img_x_bytes, img_out_bytes, img_off_bytes, img_mask_bytes;
     float offset_scale;
     int vec_bytes;                  // bytes per lane per vector
     int lanes;                      // lanes per unit (<= 64)
     int units_per_wave;
+    int cc;                         // x-gradient LDS kernel: channels per workgroup (0 = atomics path)
+    int spread;                     // x-gradient LDS kernel: pixel stride between consecutive lanes
     uint32_t units_img;
     int64_t units_total;
     FastDiv div_units_img, div_G, div_Wo;

@@ -36,89 +36,6 @@
 namespace dcnv4 {
 namespace {
 
-// Load ND consecutive dwords at a 4-byte aligned byte offset: b128 pieces,
-// and the LAST dword always on its own.  Callers may ask for one dword past
-// the data they need (a row that starts 2 bytes into a dword); keeping that
-// dword in a load of its own means no multi-dword load ever straddles the end
-// of a buffer resource, so out-of-range handling only ever zeroes whole
-// unneeded loads.
-template <int ND>
-__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* d)
-{
-    constexpr int NB = ND - 1;        // dwords before the last
-#pragma unroll
-    for (int i = 0; i + 4 <= NB; i += 4) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 4 * i), 0, 0);
-        d[i] = v.x; d[i + 1] = v.y; d[i + 2] = v.z; d[i + 3] = v.w;
-    }
-    d[ND - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * (ND - 1)), 0, 0);
-    constexpr int rem = NB % 4, b = NB - NB % 4;
-    if constexpr (rem == 1) {
-        d[b] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * b), 0, 0);
-    } else if constexpr (rem == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(voff + 4 * b), 0, 0);
-        d[b] = v.x; d[b + 1] = v.y;
-    } else if constexpr (rem == 3) {
-        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)(voff + 4 * b), 0, 0);
-        d[b] = v.x; d[b + 1] = v.y; d[b + 2] = v.z;
-    }
-}
-
-// NE elements of the I/O type starting at byte offset `start` (aligned to the
-// element size), as raw 32-bit containers: element e of a 16-bit type sits in
-// the low (e even) or high (e odd) half of word e/2; a 32-bit type in word e.
-// Two steps, so that a row can be requested one unit ahead without waiting
-// for it: issue() starts the loads, finish() (after the data is needed, one
-// pass later) moves a 16-bit row that starts 2 bytes into a dword into place.
-template <int DT, int NE>
-struct RowLoad {
-    static constexpr bool k32 = Elem<DT>::kBytes == 4;
-    static constexpr int kWords = k32 ? NE : (NE + 1) / 2;
-    // dwords loaded (16-bit types: enough to cover a 2-byte misalignment)
-    static constexpr int kLoadDwords = k32 ? NE : (2 * NE + 2 + 3) / 4;
-    uint32_t w[kWords];
-    uint32_t raw[k32 ? 1 : kLoadDwords];
-    uint32_t sh;
-
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint32_t start)
-    {
-        if constexpr (k32) {
-            load_dwords<NE>(r, start, w);
-        } else {
-            load_dwords<kLoadDwords>(r, start & ~3u, raw);
-            sh = (start & 2u) * 8u;                       // 0 or 16 bits
-        }
-    }
-
-    __device__ __forceinline__ void finish()
-    {
-        if constexpr (!k32) {
-#pragma unroll
-            for (int i = 0; i < kWords; ++i)
-                w[i] = __builtin_amdgcn_alignbit(i + 1 < kLoadDwords ? raw[i + 1] : 0u, raw[i], sh);
-        }
-    }
-
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t start)
-    {
-        issue(r, start);
-        finish();
-    }
-
-    __device__ __forceinline__ float get(int e) const
-    {
-        if constexpr (DT == DCNV4_F32) {
-            return __uint_as_float(w[e]);
-        } else if constexpr (DT == DCNV4_F16) {
-            const f16x2 h = __builtin_bit_cast(f16x2, w[e / 2]);
-            return (e & 1) ? (float)h.y : (float)h.x;
-        } else {
-            return (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
-        }
-    }
-};
-
 // Offset rows of a wave's 64 consecutive units, moved through LDS.  Per-lane
 // row loads touch 64 different cache lines per instruction (each unit's row
 // is a short piece of a pixel's row of all groups), which the texture path

@@ -80,6 +80,7 @@ def main(argv=None):
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
+    ap.add_argument("--op", default="forward", choices=("forward", "backward"))
     ap.add_argument("--command", required=True, help="the command line of the kernel-trace run")
     ap.add_argument("--counter-command", default=None,
                     help="the command line of the counter runs (COUNTER = FETCH_SIZE, then WRITE_SIZE)")
@@ -91,10 +92,14 @@ def main(argv=None):
     x_b = wl.N * wl.H * wl.W * wl.C * s
     off_b = wl.N * Ho * Wo * wl.G * 2 * wl.P * s
     m_b = wl.N * Ho * Wo * wl.G * wl.P * s
-    alg = wl.algorithmic_bytes(a.dtype)
+    alg = wl.algorithmic_bytes(a.dtype) if a.op == "forward" else wl.backward_bytes(a.dtype)
+    what = (f"x {x_b} + offset {off_b} + mask {m_b} + out {x_b}" if a.op == "forward" else
+            f"x {x_b} + offset {off_b} + mask {m_b} + grad_out {x_b} read; binary32 gradients "
+            f"{x_b * 4 // s} + {off_b * 4 // s} + {m_b * 4 // s} written")
+
     def head(cmd):
-        return [f"workload: {wl.describe(a.dtype)}",
-                f"algorithmic bytes per launch: {alg} (x {x_b} + offset {off_b} + mask {m_b} + out {x_b})",
+        return [f"workload: {wl.describe(a.dtype)} ({a.op})",
+                f"algorithmic bytes per launch: {alg} ({what})",
                 f"kernel source hash: {build.source_hash()}",
                 f"command: {cmd}", ""]
 
@@ -104,12 +109,21 @@ def main(argv=None):
         for r in st:
             lines.append(f"{r['calls']:6d} {r['avg_us']:10.3f} {r['min_us']:10.3f} {r['max_us']:10.3f} "
                          f"{r['percent']:7.2f}  {r['name'][:110]}")
-        ops = [r for r in st if is_op(r["name"])]
+        if a.op == "forward":
+            ops = [r for r in st if is_op(r["name"])]
+        else:
+            ops = [r for r in st if "k_backward" in r["name"] or "k_zero_f32" in r["name"]]
         for r in ops:
             lines.append("")
             lines.append(f"operator kernel: {r['name']}")
-            lines.append(f"  mean duration {r['avg_us']:.3f} us -> {alg / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s "
-                         f"algorithmic = {alg / (r['avg_us'] * 1e-6) / 8e12 * 100:.1f}% of 8 TB/s")
+            lines.append(f"  mean duration {r['avg_us']:.3f} us")
+        if ops:
+            launches = max(r["calls"] for r in ops)
+            per_launch = sum(r["avg_us"] * r["calls"] for r in ops) / launches
+            lines.append("")
+            lines.append(f"per launch (all kernels of one {a.op}): {per_launch:.3f} us -> "
+                         f"{alg / (per_launch * 1e-6) / 1e9:.1f} GB/s algorithmic = "
+                         f"{alg / (per_launch * 1e-6) / 8e12 * 100:.1f}% of 8 TB/s")
         with open(a.out + "_kernel_trace.txt", "w") as fh:
             fh.write("\n".join(lines) + "\n")
 

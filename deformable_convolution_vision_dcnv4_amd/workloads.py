@@ -63,6 +63,16 @@ class Workload:
         o = self.N * Ho * Wo * self.C
         return s * (x + o + self.units() * 3 * self.P)
 
+    def backward_bytes(self, dtype):
+        """Backward: x, offsets, weights and grad_out read once (I/O type);
+        grad_x, grad_offset and grad_mask written once (binary32)."""
+        s = 4 if dtype == "f32" else 2
+        Ho, Wo = self.out_hw()
+        x = self.N * self.H * self.W * self.C
+        o = self.N * Ho * Wo * self.C
+        rows = self.units() * 3 * self.P
+        return s * (x + o + rows) + 4 * (x + rows)
+
     def describe(self, dtype):
         return (f"{self.name}: N={self.N} H={self.H} W={self.W} C={self.C} "
                 f"(G={self.G}, Cg={self.Cg}) K={self.K} s{self.stride} p{self.pad} "
