@@ -71,6 +71,15 @@
  *       for a binary32 evaluation of the gradients, whose positions carry
  *       that rounding by construction.
  *
+ *   dcnv4_oracle_softmax_rows_f64 -- DCNv3's weight normalisation, which
+ *       DCNv4 removes ("不只是卷积的平替" section 1, first optimisation;
+ *       "DCNv4：重塑视觉模型核心" section 2.1; the usage guide's principle
+ *       section): a softmax over the sampling points of each (pixel, group),
+ *       so the weights are positive and sum to one.  Reading: the softmax
+ *       runs over all P points of the group, including points that fall
+ *       outside the image.  Feeding its output to the forward above gives
+ *       the DCNv3-style aggregation on the same sampling.
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
 #include <math.h>
@@ -474,5 +483,30 @@ int dcnv4_oracle_backward_f64(const double* x, const double* offset, const doubl
             }
         }
     }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* DCNv3-style weights: softmax over each group's P points (double)        */
+/* ------------------------------------------------------------------------ */
+
+/* mask: nrows rows of `stride` elements, G groups of P weights each at the
+ * start of a row; out: the same layout (only the G*P weights written).
+ * exp(m_k - max_j m_j) / sum_j exp(m_j - max_j m_j): the usual shifted form,
+ * equal to exp(m_k) / sum_j exp(m_j) and free of overflow. */
+int dcnv4_oracle_softmax_rows_f64(const double* mask, double* out, int64_t nrows, int G, int P,
+                                  int64_t stride)
+{
+    if (nrows < 0 || G < 1 || P < 1 || stride < (int64_t)G * P) return OR_ERR_ARG;
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int g = 0; g < G; ++g) {
+            const double* m = mask + r * stride + (int64_t)g * P;
+            double* o = out + r * stride + (int64_t)g * P;
+            double mx = m[0];
+            for (int k = 1; k < P; ++k) mx = m[k] > mx ? m[k] : mx;
+            double sum = 0.0;
+            for (int k = 0; k < P; ++k) sum += exp(m[k] - mx);
+            for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx) / sum;
+        }
     return OR_OK;
 }

@@ -46,6 +46,8 @@ def lib():
         L.dcnv4_oracle_forward_f64.restype = i32
         L.dcnv4_oracle_backward_f64.argtypes = [vp] * 11 + [i32] * 9 + [f64, i32, i64, i64, i32]
         L.dcnv4_oracle_backward_f64.restype = i32
+        L.dcnv4_oracle_softmax_rows_f64.argtypes = [vp, vp, i64, i32, i32, i64]
+        L.dcnv4_oracle_softmax_rows_f64.restype = i32
         for name in ("f16_to_f32_array", "bf16_to_f32_array", "f32_to_f16_array", "f32_to_bf16_array"):
             fn = getattr(L, "dcnv4_oracle_" + name)
             fn.argtypes = [vp, vp, i64]
@@ -165,6 +167,28 @@ def backward_f64(x, offset, mask, grad_out, *, K=3, stride=1, pad=1, dil=1, offs
     if bounds:
         return gx, goff, gm, dict(zip(("abs_x", "cnt_x", "abs_offset", "abs_mask"), extra))
     return gx, goff, gm
+
+
+def softmax_weights(mask, *, groups, P):
+    """DCNv3's normalisation of the weights: softmax over each group's P
+    points, per pixel, in double precision.  mask [N, Ho, Wo, >= G*P] float64."""
+    m = np.ascontiguousarray(mask, dtype=np.float64)
+    out = np.zeros_like(m)
+    N, Ho, Wo, R = m.shape
+    rc = lib().dcnv4_oracle_softmax_rows_f64(_ptr(m), _ptr(out), N * Ho * Wo, groups, P, R)
+    if rc != 0:
+        raise RuntimeError(f"oracle softmax failed with status {rc}")
+    return out
+
+
+def forward_softmax_f64(x, offset, mask, *, K=3, stride=1, pad=1, dil=1, offset_scale=1.0,
+                        remove_center=False, groups=None):
+    """The DCNv3-style aggregation: the plain definition with softmax-normalised
+    weights (double precision)."""
+    N, H, W, G, Cg, Ho, Wo, P = _dims(np.asarray(x), offset, mask, K, stride, pad, dil, remove_center, groups)
+    w = softmax_weights(mask[..., :G * P], groups=G, P=P)
+    return forward_f64(x, offset, w, K=K, stride=stride, pad=pad, dil=dil, offset_scale=offset_scale,
+                       remove_center=remove_center, groups=G)
 
 
 def to_f32(a, dtype):

@@ -43,6 +43,12 @@ MUTATIONS = {
     "bwd_scale_dropped": ("gox[s.P + k] = offset_scale * m * d_py;", "gox[s.P + k] = m * d_py;"),
     "bwd_grad_x_one_axis": ("grad_x[q + c] += m * ty * tx * go[c];", "grad_x[q + c] += m * ty * go[c];"),
     "bwd_grad_mask_abs": ("d_m += go[c] * ty * tx * f;", "d_m += fabs(go[c]) * ty * tx * f;"),
+    "sm_missing_normalisation": ("for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx) / sum;",
+                                 "for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx);"),
+    "sm_no_max_shift": ("for (int k = 0; k < P; ++k) sum += exp(m[k] - mx);\n            for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx) / sum;",
+                        "for (int k = 0; k < P; ++k) sum += exp(m[k]);\n            for (int k = 0; k < P; ++k) o[k] = exp(m[k]) / sum;"),
+    "sm_first_group_only": ("const double* m = mask + r * stride + (int64_t)g * P;",
+                            "const double* m = mask + r * stride;"),
     "f64_skips_center_always": ("if (s.remove_center && i == K / 2 && j == K / 2) continue;\n                const double dx",
                                 "if (i == K / 2 && j == K / 2) continue;\n                const double dx"),
 }
@@ -60,7 +66,8 @@ def test_planted_mistake_is_caught(name, tmp_path):
     subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC",
                     "-o", str(so), str(csrc), "-lm"], check=True, capture_output=True)
     env = dict(os.environ, DCNV4_ORACLE_LIB=str(so))
-    pins = "test_oracle_backward.py" if name.startswith("bwd_") else "test_oracle_pins.py"
+    pins = ("test_oracle_backward.py" if name.startswith("bwd_") else
+            "test_oracle_softmax.py" if name.startswith("sm_") else "test_oracle_pins.py")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-W", "ignore::RuntimeWarning",
                         os.path.join(ROOT, "tests", pins)],
