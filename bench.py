@@ -80,8 +80,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="fiit_stage1")
-    ap.add_argument("--op", default="forward", choices=("forward", "backward"),
-                    help="forward (the headline) or the backward (gradients of x, offsets, weights)")
+    ap.add_argument("--op", default="forward", choices=("forward", "backward", "softmax"),
+                    help="forward (the headline), the backward (gradients of x, offsets, weights), or "
+                         "softmax (the DCNv3-style aggregation, for comparison)")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's last)")
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotating input copies")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
@@ -156,8 +157,17 @@ def main():
                   wl.dil, wl.offset_scale, int(wl.remove_center), 0, 0, dcode, sptr) for s in sets]
         bwd = L.dcnv4_backward
 
+    if args.op == "softmax":
+        sm = L.dcnv4_forward_softmax
+        smargv = [a[:14] + (int(wl.remove_center), 0, 0) + a[14:] for a in argv]
+
     def step(i):
-        st = bwd(*bargv[i % copies]) if args.op == "backward" else fwd(*argv[i % copies])
+        if args.op == "backward":
+            st = bwd(*bargv[i % copies])
+        elif args.op == "softmax":
+            st = sm(*smargv[i % copies])
+        else:
+            st = fwd(*argv[i % copies])
         if st != 0:
             raise RuntimeError(f"dcnv4 {args.op} failed: {binding.status_string(st)}: {binding.last_error()}")
 
@@ -198,11 +208,11 @@ def main():
     log(f"per-launch event pairs: median {np.median(durs) * 1e3:.2f} us, "
         f"p10 {np.percentile(durs, 10) * 1e3:.2f} us, p90 {np.percentile(durs, 90) * 1e3:.2f} us")
 
-    alg_bytes = wl.algorithmic_bytes(dtype) if args.op == "forward" else wl.backward_bytes(dtype)
+    alg_bytes = wl.backward_bytes(dtype) if args.op == "backward" else wl.algorithmic_bytes(dtype)
     ms_per_step = wall * 1e3 / args.steps
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name if args.op == "forward" else wl.name + "_backward", dtype, alg_bytes)
+    traffic = load_traffic(wl.name if args.op == "forward" else f"{wl.name}_{args.op}", dtype, alg_bytes)
 
     cpu = None
     if not args.no_cpu_baseline and args.op == "forward":
@@ -210,8 +220,9 @@ def main():
         cpu = cpu_baseline(wl, dtype, x, off, m, args.cpu_budget)
 
     rec = {
-        "metric": ("DCNv4 fwd GB/s + Gsamples/s per MI355X; % of HBM roofline" if args.op == "forward" else
-                   "DCNv4 bwd GB/s + Gsamples/s per MI355X; % of HBM roofline"),
+        "metric": {"forward": "DCNv4 fwd GB/s + Gsamples/s per MI355X; % of HBM roofline",
+                   "backward": "DCNv4 bwd GB/s + Gsamples/s per MI355X; % of HBM roofline",
+                   "softmax": "DCNv3-style (softmax weights) fwd GB/s + Gsamples/s per MI355X; % of HBM roofline"}[args.op],
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

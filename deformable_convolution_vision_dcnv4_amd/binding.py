@@ -19,7 +19,7 @@ F32, F16, BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 # Every symbol include/dcnv4.h declares.
-EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_backward", "dcnv4_output_dim", "dcnv4_status_string",
+EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_forward_softmax", "dcnv4_backward", "dcnv4_output_dim", "dcnv4_status_string",
            "dcnv4_last_error", "dcnv4_version", "dcnv4_query_plan", "dcnv4_kernel_name")
 
 
@@ -56,6 +56,8 @@ def lib():
         L.dcnv4_forward.restype = i32
         L.dcnv4_forward_ex.argtypes = [vp, vp, vp, vp] + [i32] * 9 + [f32, i32, i64, i64, i32, vp]
         L.dcnv4_forward_ex.restype = i32
+        L.dcnv4_forward_softmax.argtypes = [vp, vp, vp, vp] + [i32] * 9 + [f32, i32, i64, i64, i32, vp]
+        L.dcnv4_forward_softmax.restype = i32
         L.dcnv4_backward.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i64, i64, i32, vp]
         L.dcnv4_backward.restype = i32
         L.dcnv4_output_dim.argtypes = [i32] * 5
@@ -136,7 +138,7 @@ def _prepare(x, offset, mask, kernel_size, remove_center, group, out):
 
 
 def forward(x, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1, offset_scale=1.0,
-            remove_center=False, group=None, out=None, stream=None):
+            remove_center=False, group=None, out=None, stream=None, softmax=False):
     """DCNv4 spatial-aggregation forward on the GPU.
 
     x       [N, H, W, G*Cg]        channels-last, contiguous
@@ -144,6 +146,8 @@ def forward(x, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1, offs
     mask    [N, Ho, Wo, >= G*P]    raw dynamic weights (no softmax)
     Returns out [N, Ho, Wo, G*Cg] in x's dtype (written into ``out`` if given).
     ``offset``/``mask`` may be views into one packed [N, Ho, Wo, 3*G*P] tensor.
+    ``softmax``: the DCNv3-style aggregation (weights softmax-normalised over
+    each group's points first).
     G defaults to offset.shape[-1] // (2*P).  The kernel runs on ``stream``
     (default: torch's current stream on x's device).
     """
@@ -165,7 +169,12 @@ def forward(x, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1, offs
             stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(x.device):
-        if not remove_center and orow == G * 2 * P and mrow == G * P:
+        if softmax:
+            _check(lib().dcnv4_forward_softmax(x.data_ptr(), optr, mptr, out.data_ptr(), N, H, W, G, C // G,
+                                               K, stride, pad, dilation, float(offset_scale),
+                                               1 if remove_center else 0, orow, mrow,
+                                               _DTYPE_CODE[x.dtype], sptr))
+        elif not remove_center and orow == G * 2 * P and mrow == G * P:
             _check(lib().dcnv4_forward(x.data_ptr(), optr, mptr, out.data_ptr(), N, H, W, G, C // G,
                                        K, stride, pad, dilation, float(offset_scale),
                                        _DTYPE_CODE[x.dtype], sptr))

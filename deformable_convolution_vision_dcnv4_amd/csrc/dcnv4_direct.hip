@@ -68,7 +68,7 @@ __device__ __forceinline__ void store_raw(void* out, int64_t elem, const float* 
     *reinterpret_cast<V*>(static_cast<S*>(out) + elem) = o;
 }
 
-template <int DT, int VB, int KT>
+template <int DT, int VB, int KT, int SM>
 __global__ void __launch_bounds__(256)
 k_direct(KArgs a)
 {
@@ -104,6 +104,15 @@ k_direct(KArgs a)
 #pragma unroll
     for (int c = 0; c < NE; ++c) acc[c] = 0.0f;
 
+    // DCNv3-style weights (SM): w_k = exp(m_k - max) / sum_j exp(m_j - max),
+    // the sum in point order, exp recomputed identically in the main loop
+    float mx = 0.0f, rs = 0.0f;
+    if (SM) {
+        mx = E::to_f(ms[0]);
+        for (int k = 1; k < P; ++k) mx = fmaxf(mx, E::to_f(ms[k]));
+        for (int k = 0; k < P; ++k) rs += expf(E::to_f(ms[k]) - mx);
+    }
+
     const float fW = (float)a.W, fH = (float)a.H;
     const int bx0 = (int)wo * a.stride - a.pad;
     const int by0 = (int)ho * a.stride - a.pad;
@@ -114,7 +123,8 @@ k_direct(KArgs a)
         if (a.remove_center && q == center) continue;
         const int k = (a.remove_center && q > center) ? q - 1 : q;
         const int i = q / K, j = q - (q / K) * K;
-        const PointCoef c = point_coef(E::to_f(os[k]), E::to_f(os[P + k]), E::to_f(ms[k]),
+        const float mk = SM ? expf(E::to_f(ms[k]) - mx) / rs : E::to_f(ms[k]);
+        const PointCoef c = point_coef(E::to_f(os[k]), E::to_f(os[P + k]), mk,
                                        a.offset_scale, (float)(bx0 + j * a.dil), (float)(by0 + i * a.dil),
                                        fW, fH);
         // bitwise & and precomputed candidates: the corner reads carry no branch
@@ -139,13 +149,20 @@ k_direct(KArgs a)
     store_raw<DT, VB>(a.out, (int64_t)n * a.img_out_elems + (int64_t)pix * a.C + g * a.Cg + lane_in_unit * NE, acc);
 }
 
+template <int DT, int VB, int SM>
+void launch_k(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+{
+    if (a.K == 3)
+        hipLaunchKernelGGL((k_direct<DT, VB, 3, SM>), dim3((unsigned)grid), dim3(block), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_direct<DT, VB, 0, SM>), dim3((unsigned)grid), dim3(block), 0, stream, a);
+}
+
 template <int DT, int VB>
 hipError_t launch_vb(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
-    if (a.K == 3)
-        hipLaunchKernelGGL((k_direct<DT, VB, 3>), dim3((unsigned)grid), dim3(block), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_direct<DT, VB, 0>), dim3((unsigned)grid), dim3(block), 0, stream, a);
+    if (a.softmax) launch_k<DT, VB, 1>(a, block, grid, stream);
+    else launch_k<DT, VB, 0>(a, block, grid, stream);
     return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* m
     p->x = x; p->off = offset; p->msk = mask; p->out = (void*)out;
     p->N = N; p->H = H; p->W = W; p->G = G; p->Cg = Cg; p->K = K; p->P = P;
     p->stride = stride; p->pad = pad; p->dil = dil; p->Ho = Ho; p->Wo = Wo;
-    p->remove_center = remove_center; p->off_row = offset_row; p->mask_row = mask_row;
+    p->remove_center = remove_center; p->softmax = 0; p->off_row = offset_row; p->mask_row = mask_row;
     p->offset_scale = offset_scale; p->dtype = dtype;
     if (N == 0 || !check_pointers) return DCNV4_OK;
 
@@ -151,11 +151,12 @@ int check_device()
 int forward_impl(const void* x, const void* offset, const void* mask, void* out,
                  int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,
                  float offset_scale, int remove_center, int64_t offset_row, int64_t mask_row,
-                 int dtype, void* stream)
+                 int dtype, void* stream, int softmax = 0)
 {
     dcnv4::Problem p;
     int st = validate(&p, x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dil,
                       offset_scale, remove_center, offset_row, mask_row, dtype);
+    p.softmax = softmax;
     if (st != DCNV4_OK || N == 0) return st;
     st = check_device();
     if (st != DCNV4_OK) return st;
@@ -255,6 +256,16 @@ int dcnv4_forward_ex(const void* x, const void* offset, const void* mask, void* 
 {
     return forward_impl(x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dilation,
                         offset_scale, remove_center, offset_row, mask_row, dtype, stream);
+}
+
+int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, void* out,
+                          int N, int H, int W, int G, int Cg,
+                          int K, int stride, int pad, int dilation, float offset_scale,
+                          int remove_center, int64_t offset_row, int64_t mask_row,
+                          int dtype, void* stream)
+{
+    return forward_impl(x, offset, mask, out, N, H, W, G, Cg, K, stride, pad, dilation,
+                        offset_scale, remove_center, offset_row, mask_row, dtype, stream, 1);
 }
 
 int dcnv4_output_dim(int in, int K, int stride, int pad, int dilation)

@@ -16,6 +16,7 @@ struct Problem {
     void* out;
     int N, H, W, G, Cg, K, P, stride, pad, dil, Ho, Wo;
     int remove_center;
+    int softmax;            // DCNv3-style: softmax over each group's P weights first
     int64_t off_row, mask_row;
     float offset_scale;
     int dtype;

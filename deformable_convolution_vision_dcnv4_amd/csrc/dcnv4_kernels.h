@@ -39,6 +39,7 @@ struct KArgs {
     void* out;
     int H, W, G, Cg, C, K, P, stride, pad, dil, Ho, Wo;
     int remove_center;
+    int softmax;                    // weights normalised by a softmax over each group's points
     int64_t off_row, mask_row;      // elements between output pixels
     uint32_t img_x_bytes;           // one image of x
     uint32_t img_off_bytes;         // one image of offsets (rows of its last pixel included)

@@ -221,7 +221,8 @@ void plan_direct(const Problem& p, Plan* pl)
 void make_plan(const Problem& p, Plan* plan)
 {
     const Tune& t = tune();
-    if (t.kernel != 1 && plan_window(p, plan)) return;
+    // the softmax variant runs on the direct kernel only
+    if (t.kernel != 1 && !p.softmax && plan_window(p, plan)) return;
     plan_direct(p, plan);
 }
 
@@ -233,7 +234,7 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
     a.x = p.x; a.off = p.off; a.msk = p.msk; a.out = p.out;
     a.H = p.H; a.W = p.W; a.G = p.G; a.Cg = p.Cg; a.C = p.G * p.Cg;
     a.K = p.K; a.P = p.P; a.stride = p.stride; a.pad = p.pad; a.dil = p.dil;
-    a.Ho = p.Ho; a.Wo = p.Wo; a.remove_center = p.remove_center;
+    a.Ho = p.Ho; a.Wo = p.Wo; a.remove_center = p.remove_center; a.softmax = p.softmax;
     a.off_row = p.off_row; a.mask_row = p.mask_row;
     a.offset_scale = p.offset_scale;
     a.img_x_elems = (int64_t)p.H * p.W * a.C;

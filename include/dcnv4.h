@@ -113,6 +113,24 @@ int dcnv4_forward_ex(const void* x, const void* offset, const void* mask, void* 
                      int dtype, void* stream);
 
 /*
+ * The DCNv3-style aggregation on the same sampling, for comparison: the
+ * weights of each (pixel, group) pass through a softmax over their P points
+ * before use -- the normalisation DCNv4 removes ("不只是卷积的平替"
+ * (jsqmd.com/news/933833) section 1, first optimisation; bqwf.cn/news/1148139
+ * section 2.1).  The softmax covers all P points, in or out of the image.
+ * Arguments as dcnv4_forward_ex.  Arithmetic: mx = max_k m_k; S = sum over k
+ * in order of expf(m_k - mx); w_k = expf(m_k - mx) / S (IEEE division), then
+ * the operation sequence above with w_k as the weight.  expf is the device
+ * library's, so results match a reference to within its error, not bit for
+ * bit.  Runs on the general (direct) kernel.
+ */
+int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, void* out,
+                          int N, int H, int W, int G, int Cg,
+                          int K, int stride, int pad, int dilation, float offset_scale,
+                          int remove_center, int64_t offset_row, int64_t mask_row,
+                          int dtype, void* stream);
+
+/*
  * Gradients of the operator (dcnv4_forward_ex's arguments) given grad_out =
  * dL/dout [N, Ho, Wo, G*Cg] in the I/O type.  The forward is
  *   out = sum_k m_k * sum_q tri(py_k - qy) tri(px_k - qx) x[q],
