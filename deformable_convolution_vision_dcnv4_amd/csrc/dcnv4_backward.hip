@@ -25,7 +25,6 @@
 
 #include <string.h>
 
-#include <numeric>
 
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
@@ -205,20 +204,30 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a)
 }
 
 // x's gradient of one (image, group, chunk of CC channels), accumulated in an
-// LDS copy of the zero-bordered image [-1, H] x [-1, W] (binary32, one plane
-// per channel, so that lanes on neighbouring pixels add to different banks):
-// every corner of every valid point lands inside it, corners off the image
-// land on the border, which is dropped.  The workgroup owns that
+// LDS copy of the zero-bordered image [-1, H] x [-1, W] (one plane per
+// channel): every corner of every valid point lands inside it, corners off
+// the image land on the border, which is dropped.  The workgroup owns that
 // slice of grad_x, so it is written once with plain stores: no global
-// atomics and no separate zeroing.  LDS adds from different lanes to one
-// pixel happen in no fixed order.
+// atomics and no separate zeroing.
+//
+// The accumulation is in 64-bit fixed point with LDS integer atomic adds
+// (binary32 LDS atomic adds run tens of times slower on this GPU).  Each
+// term t = w * g (binary32, as the float path computes it) becomes
+// rint(t * 2^F); F is fixed per (image, group) so that no sum can overflow:
+// with M = max|m| * max|g| over the (image, group) (|t| <= M) and at most
+// 2^cbits terms per element, F = 62 - cbits - e where M < 2^e.  Integer sums
+// do not depend on the order of the adds, so x's gradient is reproducible;
+// each term is off by at most 2^-(F+1).  An (image, group) whose weights or
+// output gradient hold a non-finite value uses binary32 LDS atomic adds.
 template <int DT, int RC, int CC>
 __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
 {
     using E = Elem<DT>;
     constexpr int s = E::kBytes;
     constexpr int P = 9 - RC;                 // K = 3
-    extern __shared__ float acc[];
+    extern __shared__ unsigned long long acc[];
+    __shared__ float red[2][16];
+    __shared__ bool flag[16];
     const int chunks = a.Cg / CC;
     const uint32_t b = blockIdx.x;
     const uint32_t n = b / (uint32_t)(a.G * chunks);
@@ -226,8 +235,7 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
     const uint32_t g = r / (uint32_t)chunks, ch = r - g * (uint32_t)chunks;
     const int WP = a.W + 2;                                  // bordered row
     const int plane = (a.H + 2) * WP;
-    for (int i = threadIdx.x; i < plane * CC; i += blockDim.x) acc[i] = 0.0f;
-    __syncthreads();
+    for (int i = threadIdx.x; i < plane * CC; i += blockDim.x) acc[i] = 0ull;
 
     const char* oimg = static_cast<const char*>(a.off) + (int64_t)n * a.img_off_elems * s;
     const char* mimg = static_cast<const char*>(a.msk) + (int64_t)n * a.img_mask_elems * s;
@@ -235,14 +243,62 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(oimg, a.img_off_bytes);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(mimg, a.img_mask_bytes);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gimg, a.img_out_bytes);
-    const float fW = (float)a.W, fH = (float)a.H;
     const int npix = a.Ho * a.Wo;
-    // lanes of a wave take pixels `spread` apart (spread coprime with npix, so
-    // t -> t * spread mod npix visits every pixel once): their corners rarely
-    // coincide, and coinciding LDS atomic adds in one instruction serialise
-    const uint32_t spread = (uint32_t)a.spread;
-    for (int t = threadIdx.x; t < npix; t += blockDim.x) {
-        const int pix = (int)(((uint64_t)t * spread) % (uint32_t)npix);
+
+    // ---- the scale: max|m| and max|g| over the (image, group); a non-finite
+    // value (which a maximum would skip for NaN) is flagged on its own
+    float mm = 0.0f, mg = 0.0f;
+    bool bad = false;
+    for (int pix = threadIdx.x; pix < npix; pix += blockDim.x) {
+        RowLoad<DT, P> mrow;
+        mrow.load(rm, (uint32_t)(((int64_t)pix * a.mask_row + (int64_t)g * P) * s));
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const float v = mrow.get(k);
+            mm = fmaxf(mm, fabsf(v));
+            bad |= !isfinite(v);
+        }
+        const uint32_t gstart = (uint32_t)(((int64_t)pix * a.C + (int64_t)g * a.Cg) * s);
+        for (int c0 = 0; c0 < a.Cg; c0 += 16) {
+            RowLoad<DT, 16> gl;
+            gl.load(rg, gstart + (uint32_t)(c0 * s));
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                if (c0 + c < a.Cg) {
+                    const float v = gl.get(c);
+                    mg = fmaxf(mg, fabsf(v));
+                    bad |= !isfinite(v);
+                }
+            }
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        mm = fmaxf(mm, __shfl_xor(mm, off));
+        mg = fmaxf(mg, __shfl_xor(mg, off));
+    }
+    const bool wave_bad = __any(bad);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { red[0][wave] = mm; red[1][wave] = mg; flag[wave] = wave_bad; }
+    __syncthreads();
+    mm = 0.0f; mg = 0.0f;
+    bool fixed = true;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        mm = fmaxf(mm, red[0][w]);
+        mg = fmaxf(mg, red[1][w]);
+        fixed = fixed & !flag[w];
+    }
+    const float M = mm * mg;
+    fixed = fixed & isfinite(M);
+    int F = 0;
+    if (fixed && M > 0.0f) {
+        int e;
+        frexpf(M, &e);                        // M < 2^e
+        F = 62 - a.cbits - e;
+    }
+
+    const float fW = (float)a.W, fH = (float)a.H;
+    float* accf = reinterpret_cast<float*>(acc);
+    for (int pix = threadIdx.x; pix < npix; pix += blockDim.x) {
         const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
         // the unit's offset, weight and output-gradient rows: all loads in flight together
         RowLoad<DT, 2 * P> orow;
@@ -268,16 +324,32 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
             const float lx = px - fx, ly = py - fy;
             const float hx = 1.0f - lx, hy = 1.0f - ly;
             const float mhy = m * hy, mly = m * ly;
-            const float w00 = mhy * hx, w01 = mhy * lx, w10 = mly * hx, w11 = mly * lx;
+            const float w[4] = {mhy * hx, mhy * lx, mly * hx, mly * lx};
+            const int cell[4] = {0, 1, WP, WP + 1};
             // corner (y0, x0) of the bordered image; the others follow
-            float* c00 = acc + (y0 + 1) * WP + (x0 + 1);
+            const int c00 = (y0 + 1) * WP + (x0 + 1);
 #pragma unroll
-            for (int c = 0; c < CC; ++c) {
-                float* pc = c00 + c * plane;
-                atomicAdd(pc, w00 * gr[c]);
-                atomicAdd(pc + 1, w01 * gr[c]);
-                atomicAdd(pc + WP, w10 * gr[c]);
-                atomicAdd(pc + WP + 1, w11 * gr[c]);
+            for (int cr = 0; cr < 4; ++cr) {
+#pragma unroll
+                for (int c = 0; c < CC; ++c) {
+                    const float t = w[cr] * gr[c];
+                    const int idx = c * plane + c00 + cell[cr];
+                    if (fixed) {
+                        // rint(t * 2^F) as a two's-complement 64-bit integer, from the
+                        // magnitude's high and low 32-bit parts (both exact in binary32:
+                        // below 2^32 the magnitude is an integer < 2^32, above it a
+                        // multiple of 2^9)
+                        const float qf = rintf(ldexpf(t, F));
+                        const float mag = fabsf(qf);
+                        const float hi = floorf(mag * 0x1p-32f);
+                        const float lo = mag - hi * 0x1p32f;
+                        const unsigned long long u =
+                            ((unsigned long long)(uint32_t)hi << 32) + (unsigned long long)(uint32_t)lo;
+                        atomicAdd(&acc[idx], qf < 0.0f ? 0ull - u : u);
+                    } else {
+                        atomicAdd(&accf[idx], t);
+                    }
+                }
             }
         }
     }
@@ -289,7 +361,8 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
     for (int i = threadIdx.x; i < interior; i += blockDim.x) {
         const int c = i % CC, p = i / CC;
         const int y = p / a.W, x = p - (p / a.W) * a.W;
-        gx[(int64_t)p * a.C + c] = acc[c * plane + (y + 1) * WP + (x + 1)];
+        const int idx = c * plane + (y + 1) * WP + (x + 1);
+        gx[(int64_t)p * a.C + c] = fixed ? (float)ldexp((double)(long long)acc[idx], -F) : accf[idx];
     }
 }
 
@@ -407,13 +480,13 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
         if (e != hipSuccess) return e;
     }
     if (a.cc) {
-        // the smallest stride >= 13 coprime with the pixel count
-        const int64_t npix = (int64_t)p.Ho * p.Wo;
-        int sp = 13;
-        while (std::gcd((int64_t)sp, npix) != 1) ++sp;
-        a.spread = npix > 1 ? sp : 1;
+        // terms per x element: at most (units of the image) * P points * 4 corners
+        const int64_t terms = (int64_t)p.Ho * p.Wo * p.P * 4;
+        int cb = 0;
+        while (((int64_t)1 << cb) < terms) ++cb;
+        a.cbits = cb;
         const unsigned grid = (unsigned)((int64_t)p.N * p.G * (p.Cg / a.cc));
-        const size_t lds = (size_t)(p.H + 2) * (p.W + 2) * a.cc * 4;
+        const size_t lds = (size_t)(p.H + 2) * (p.W + 2) * a.cc * 8;
         switch (p.dtype) {
             case DCNV4_F32: launch_bx<DCNV4_F32>(a, grid, lds, stream); break;
             case DCNV4_F16: launch_bx<DCNV4_F16>(a, grid, lds, stream); break;
@@ -428,9 +501,9 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
 int backward_x_chunk(const Problem& p)
 {
     // K = 3: the most channels (a power of two dividing Cg, at most 16) whose
-    // bordered image fits in LDS
+    // bordered image of 64-bit accumulators fits in LDS
     if (p.K != 3) return 0;
-    const int64_t cell = (int64_t)(p.H + 2) * (p.W + 2) * 4;
+    const int64_t cell = (int64_t)(p.H + 2) * (p.W + 2) * 8;
     for (int cc = 16; cc >= 1; cc /= 2)
         if (p.Cg % cc == 0 && cell * cc <= kLdsPerCu) return cc;
     return 0;

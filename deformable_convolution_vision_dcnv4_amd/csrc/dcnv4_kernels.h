@@ -91,7 +91,7 @@ struct BArgs {
     int lanes;                      // lanes per unit (<= 64)
     int units_per_wave;
     int cc;                         // x-gradient LDS kernel: channels per workgroup (0 = atomics path)
-    int spread;                     // x-gradient LDS kernel: pixel stride between consecutive lanes
+    int cbits;                      // x-gradient LDS kernel: log2 bound of the terms per element
     uint32_t units_img;
     int64_t units_total;
     FastDiv div_units_img, div_G, div_Wo;

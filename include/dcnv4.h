@@ -145,9 +145,13 @@ int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, v
  *                only the G*2*P gradient elements of each row are written
  *   grad_mask    rows of mask_row elements, like mask; G*P elements written
  * Any gradient pointer may be NULL (not computed).  Arithmetic is binary32;
- * grad_offset and grad_mask are summed in a fixed order (reproducible);
- * grad_x is accumulated with hardware atomic adds, whose order is not fixed
- * (results may differ in the last bits between runs).  Gradients must not
+ * grad_offset and grad_mask are summed in a fixed order (reproducible).
+ * grad_x: for K = 3 when a few channels of the zero-bordered image fit in
+ * LDS, each term w*g is rounded to a multiple of 2^-F and summed exactly in
+ * 64-bit integers (reproducible; F per (image, group) from the largest
+ * |weight| * |grad_out| and the term count, so sums cannot overflow; the
+ * binary32 path if either holds a non-finite value); otherwise summed with
+ * hardware atomic adds, whose order is not fixed.  Gradients must not
  * overlap the inputs or grad_x; grad_offset and grad_mask may interleave
  * (one packed tensor) but must not share elements.  Needs Cg*s <= 64 vectors
  * of the widest width the pointers allow (else DCNV4_ERR_TOO_LARGE).

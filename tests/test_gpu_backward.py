@@ -7,9 +7,12 @@ The GPU evaluates them in binary32; with u = 2^-24, each gradient element is
 a sum of n products of a few rounded factors, so its error is bounded by
 (n + c) * u * (sum of the terms' absolute values), first order, in any
 summation order.  The oracle returns those absolute sums and term counts:
-  grad_x       n = number of scattered terms (order not fixed: atomics), c = 6
+  grad_x       n = number of scattered terms, c = 6
   grad_mask    n = 4*Cg products per point, c = 8
   grad_offset  n = 4*Cg products of differences per point, c = 10
+For K = 3 x's gradient is summed in 64-bit fixed point (each term rounded to
+a multiple of 2^-F, F fixed per (image, group) from max|m| * max|g| and the
+term-count bound, as the kernel states): each term adds at most 2^-(F+1).
 """
 import numpy as np
 import pytest
@@ -43,6 +46,27 @@ def grad_out_for(wl, dtype, seed):
     return g
 
 
+def fixed_point_quantum(wl, m32, go32):
+    """Per-element bound of the fixed-point rounding of x's gradient: 2^-(F+1)
+    with F = 62 - cbits - e, M = max|m| * max|g| over the (image, group) in
+    binary32, M < 2^e (as the LDS kernel computes it); shaped like x."""
+    G, P, Cg = wl.G, wl.P, wl.Cg
+    Ho, Wo = wl.out_hw()
+    cbits = int(np.ceil(np.log2(Ho * Wo * P * 4)))
+    q = np.zeros((wl.N, 1, 1, G * Cg))
+    for n in range(wl.N):
+        for g in range(G):
+            mm = np.float32(np.abs(m32[n, ..., g * P:(g + 1) * P]).max())
+            mg = np.float32(np.abs(go32[n, ..., g * Cg:(g + 1) * Cg]).max())
+            M = np.float32(mm * mg)
+            F = 0
+            if M > 0:
+                _, e = np.frexp(M)
+                F = 62 - cbits - int(e)
+            q[n, 0, 0, g * Cg:(g + 1) * Cg] = 2.0 ** (-(F + 1))
+    return q
+
+
 def check(wl, dtype, seed=41, packed=False):
     x, off, m = gen.make_inputs(wl, dtype)
     go = grad_out_for(wl, dtype, seed)
@@ -64,6 +88,8 @@ def check(wl, dtype, seed=41, packed=False):
     torch.cuda.synchronize()
     gx, goff, gm = (t.cpu().numpy().astype(np.float64) for t in (gx, goff, gm))
     tol_x = (b["cnt_x"] + 6) * U * b["abs_x"] + 1e-300
+    if wl.K == 3:
+        tol_x = tol_x + b["cnt_x"] * fixed_point_quantum(wl, ref.to_f32(m, dtype), ref.to_f32(go, dtype))
     tol_m = (4 * wl.Cg + 8) * U * b["abs_mask"] + 1e-300
     tol_o = (4 * wl.Cg + 10) * U * b["abs_offset"] + 1e-300
     ex, em, eo = np.abs(gx - gx_ref), np.abs(gm - gm_ref), np.abs(goff - goff_ref)
@@ -111,8 +137,25 @@ def test_backward_offset_and_mask_gradients_are_reproducible():
     r1 = binding.backward(*args)
     r2 = binding.backward(*args)
     torch.cuda.synchronize()
-    assert torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
-    assert torch.allclose(r1[0], r2[0], rtol=1e-5, atol=1e-6)
+    # all three: x's gradient (K = 3) is summed in fixed point, order-independent
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
+
+
+def test_backward_non_finite_weight_propagates():
+    """A NaN weight: that (image, group) takes the binary32 path and the NaN
+    reaches exactly the pixels the oracle's gradient has NaN at."""
+    wl = Workload("bwd_nan", 2, 10, 11, 2, 8, ("f32",), offset_dist=("normal", 1.5), seed=50)
+    x, off, m = gen.make_inputs(wl, "f32")
+    go = grad_out_for(wl, "f32", 51)
+    m = m.copy()
+    m[1, 4, 5, 9 + 3] = np.nan                # image 1, group 1, point 3
+    gx, goff, gm = binding.backward(*(gu.dev(a, "f32") for a in (x, off, m, go)))
+    torch.cuda.synchronize()
+    gx = gx.cpu().numpy().astype(np.float64)
+    want, _, _ = ref.backward_f64(*(a.astype(np.float64) for a in (x, off, m, go)), f32_positions=True)
+    assert np.array_equal(np.isnan(gx), np.isnan(want)) and np.isnan(want).any()
+    fin = ~np.isnan(want)
+    assert np.max(np.abs(gx[fin] - want[fin])) < 1e-4
 
 
 def test_backward_points_outside_have_zero_gradient():
