@@ -30,6 +30,8 @@
 // XCDs round-robin) receives a contiguous run of tiles: neighbouring tiles
 // and the groups of one tile share that XCD's L2.
 
+#include <type_traits>
+
 #include "dcnv4_device.h"
 #include "dcnv4_kernels.h"
 
@@ -44,14 +46,19 @@ namespace {
 // lanes of one load cover whole rows dword by dword, and the load unit writes
 // each dword straight to LDS at position q (no registers held while in
 // flight), so unit u's row lands at dwords [u*ND, u*ND + ND) of the wave's
-// buffer, from where its lane reads it back.  `base` = byte offset of the
-// first unit's row; consecutive units' rows are `row_bytes` apart.
+// buffer, from where its lane reads it back.  `rows` holds `rows_bytes`
+// bytes of rows (one image's); `base` = byte offset of the first unit's row
+// there; consecutive units' rows are `row_bytes` apart.  Rows past the end
+// (or a base past it) read as zeros.
 template <int ND>
-__device__ __forceinline__ void stage_offset_rows(__amdgpu_buffer_rsrc_t ro, uint32_t* wbuf, uint32_t lane,
-                                                  uint32_t base, uint32_t row_bytes)
+__device__ __forceinline__ void stage_offset_rows(const char* rows, uint32_t rows_bytes, uint32_t* wbuf,
+                                                  uint32_t lane, uint32_t base, uint32_t row_bytes)
 {
-    // the same for every lane of the wave: a scalar offset
+    // the same for every lane of the wave, and folded into the resource's
+    // base address: the range check covers the per-lane offsets only
     base = __builtin_amdgcn_readfirstlane(base);
+    const uint32_t left = __builtin_amdgcn_readfirstlane(base < rows_bytes ? rows_bytes - base : 0u);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(rows + base, left);
     // recomputed at each call (a few integer operations per load) instead of
     // keeping ND loop-invariant offsets in registers across the whole loop
     asm volatile("" : "+v"(lane));
@@ -62,7 +69,7 @@ __device__ __forceinline__ void stage_offset_rows(__amdgpu_buffer_rsrc_t ro, uin
     for (int k = 0; k < ND; ++k) {
         // u < 64 and a row is < 2^24 bytes (the caller checks): 24-bit multiply
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(wbuf + k * 64),
-                                                 4, (int)(__umul24(u, row_bytes) + 4u * d), (int)base, 0, 0);
+                                                 4, (int)(__umul24(u, row_bytes) + 4u * d), 0, 0, 0);
         d += dd;
         u += du;
         if (d >= (uint32_t)ND) { d -= ND; ++u; }
@@ -344,7 +351,8 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     // flight across the barrier
     auto first_rows = [&]() {
         if (COAL) {
-            stage_offset_rows<ND>(ro, wbuf, lane, off_tile_base + (threadIdx.x - lane) * off_row_bytes, off_row_bytes);
+            stage_offset_rows<ND>(os_img, a.img_off_bytes, wbuf, lane,
+                                  off_tile_base + (threadIdx.x - lane) * off_row_bytes, off_row_bytes);
             if (threadIdx.x < units) msk.issue(rm, lin_sm);
         } else if (threadIdx.x < units) {
             int oy, ox, gl;
@@ -433,7 +441,15 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     // units whose points leave a partial window, one bit per pass: finished
     // after the main loop, with every corner read from global memory
     uint64_t fbmask = 0;
-    for (uint32_t pass = 0; u < units; u += B, ++pass) {
+    // One unit per lane.  NEXT: the unit's lane has another pass, whose rows
+    // are requested during this one.  Coalesced variant: the passes with a
+    // successor run in a loop whose loads and stores are the same on every
+    // path, and the wave's last pass follows it; with the first unit's rows
+    // waited for here, the compiler's own waits at the top of a unit then
+    // leave its predecessor's stores in flight.
+    if (COAL) wait_vmem_at_most<0>();
+    auto unit_pass = [&](auto next_tag, uint32_t pass) {
+        constexpr bool NEXT = decltype(next_tag)::value;
         int oy, ox, gl;
         if (COAL) {
             oy = lin_oy; ox = lin_ox; gl = 0;
@@ -457,29 +473,42 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         }
         RowLoad<DT, P> cm = msk;
         cm.finish();
-        // the next unit's rows are requested now and land while this unit computes
+        // the rows just read are unpacked here, before the next unit's rows
+        // are requested into the same registers: a read of them sunk below
+        // that request would keep both sets alive and force a copy of rows in
+        // flight at the end of the unit (a wait for every load and store)
+        if (COAL) {
+#pragma unroll
+            for (int i = 0; i < RowLoad<DT, P>::kWords; ++i) asm volatile("" : "+v"(cm.w[i]));
+        }
+
+        // the next unit's rows are requested now and land while this unit
+        // computes (without a per-lane test in the coalesced variant: rows
+        // past the image read as zeros and are never used)
         uint32_t nso = 0, nsm = 0;
         const bool more = u + B < units;
-        if (COAL && u - lane + B < units)
-            stage_offset_rows<ND>(ro, wbuf, lane, off_tile_base + (u - lane + B) * off_row_bytes, off_row_bytes);
+        if (COAL && NEXT)
+            stage_offset_rows<ND>(os_img, a.img_off_bytes, wbuf, lane, off_tile_base + (u - lane + B) * off_row_bytes,
+                                  off_row_bytes);
         fence_sched();
         uint32_t oo = 0;
         if (COAL) {
             oo = lin_oo;
-            if (more) msk.issue(rm, lin_sm + B * mask_row_bytes);
+            if (NEXT) msk.issue(rm, lin_sm + B * mask_row_bytes);
             lin_sm += B * mask_row_bytes;
             lin_oo += B * (uint32_t)a.C * s;
             lin_ox += (int)lin_dox;
             lin_oy += (int)lin_doy;
             if (lin_ox >= a.Wo) { lin_ox -= a.Wo; ++lin_oy; }
-        } else if (more) {
+        } else if (NEXT && more) {
             int oy2, ox2, gl2;
             unit_of(u + B, oy2, ox2, gl2);
             row_starts(min(oy2, a.Ho - 1), min(ox2, a.Wo - 1), gl2, nso, nsm);
             offs.issue(ro, nso);
             msk.issue(rm, nsm);
         }
-        if (oy >= a.Ho || ox >= a.Wo) continue;
+        // (a whole-image window's units all lie inside the image)
+        if (!FULL && (oy >= a.Ho || ox >= a.Wo)) return;
         const int g = g0 + gl;
 
         float acc[NC];
@@ -519,6 +548,15 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
+    };
+    uint32_t pass = 0;
+    if (COAL) {
+        // u - lane: the wave's first unit of this pass (the same in every lane)
+        for (; u - lane + B < units; u += B, ++pass) unit_pass(std::true_type{}, pass);
+        if (u < units) unit_pass(std::false_type{}, pass);
+    } else {
+        // (per-lane requests of the next unit's rows, see `more`)
+        for (; u < units; u += B, ++pass) unit_pass(std::true_type{}, pass);
     }
 
     if (!FULL) {
