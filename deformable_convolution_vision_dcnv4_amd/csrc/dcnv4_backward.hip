@@ -82,7 +82,7 @@ __device__ __forceinline__ float unit_sum(float v, int L, int lane0)
 }
 
 template <int DT, int VB, int KT>
-__global__ void __launch_bounds__(256) k_backward(BArgs a)
+__global__ void __launch_bounds__(256) k_backward(BArgs a, uint32_t total_blocks, uint32_t per_xcd)
 {
     using E = Elem<DT>;
     using S = typename E::S;
@@ -96,7 +96,10 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int uiw = lane / L;                  // unit in wave
     const int lane_in_unit = lane - uiw * L;
-    const int64_t ublk = (int64_t)blockIdx.x * 4 * upw;
+    // blocks renumbered per XCD as in the direct forward kernel (per_xcd > 0)
+    uint32_t lb = blockIdx.x;
+    if (per_xcd && !logical_block(blockIdx.x, total_blocks, per_xcd, &lb)) return;
+    const int64_t ublk = (int64_t)lb * 4 * upw;
     const int64_t unit_g = ublk + (int64_t)wave * upw + uiw;
     const bool active = uiw < upw && unit_g < a.units_total;
     const int lane0 = uiw * L;
@@ -388,10 +391,14 @@ void launch_bx(const BArgs& a, unsigned grid, size_t lds, hipStream_t stream)
 template <int DT, int VB>
 void launch_vb(const BArgs& a, int64_t grid, hipStream_t stream)
 {
+    // each XCD a contiguous range of blocks when an image fits in its L2 (4 MB)
+    const uint32_t total = (uint32_t)grid;
+    const uint32_t per_xcd = a.img_x_bytes <= (4u << 20) ? (total + 7) / 8 : 0u;
+    const uint32_t launched = per_xcd ? per_xcd * 8 : total;
     if (a.K == 3)
-        hipLaunchKernelGGL((k_backward<DT, VB, 3>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_backward<DT, VB, 3>), dim3(launched), dim3(256), 0, stream, a, total, per_xcd);
     else
-        hipLaunchKernelGGL((k_backward<DT, VB, 0>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_backward<DT, VB, 0>), dim3(launched), dim3(256), 0, stream, a, total, per_xcd);
 }
 
 template <int DT>

@@ -29,6 +29,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin, each XCD with its own L2.
+// A grid of 8 * per_xcd workgroups renumbered so that XCD x runs the
+// contiguous logical range [x * per_xcd, (x + 1) * per_xcd): neighbouring
+// tiles share an L2.  Decodes workgroup b; false for the padding workgroups
+// that round the grid up to a multiple of 8.
+__device__ __forceinline__ bool logical_block(uint32_t b, uint32_t total, uint32_t per_xcd, uint32_t* out)
+{
+    const uint32_t xcd = b & 7u, k = b >> 3;
+    const uint32_t l = xcd * per_xcd + k;
+    *out = l;
+    return k < per_xcd && l < total;
+}
+
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);

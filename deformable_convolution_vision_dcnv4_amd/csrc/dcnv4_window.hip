@@ -88,16 +88,6 @@ __device__ __forceinline__ void wait_vmem_at_most() { __builtin_amdgcn_s_waitcnt
 // Buffer loads issued by load_dwords<ND>.
 template <int ND> constexpr int kDwordLoads = (ND - 1) / 4 + ((ND - 1) % 4 != 0) + 1;
 
-// Decode the renumbered workgroup id into its logical tile index; false for
-// the padding workgroups that round the grid up to a multiple of 8.
-__device__ __forceinline__ bool logical_block(uint32_t b, uint32_t total, uint32_t per_xcd, uint32_t* out)
-{
-    const uint32_t xcd = b & 7u, k = b >> 3;
-    const uint32_t l = xcd * per_xcd + k;
-    *out = l;
-    return k < per_xcd && l < total;
-}
-
 // Corner data and weights of one sampling point, in flight.
 template <int NV>
 struct PointRegs {
