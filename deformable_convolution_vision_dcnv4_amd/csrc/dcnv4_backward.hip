@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a, uint32_t total_blocks
 // each term is off by at most 2^-(F+1).  An (image, group) whose weights or
 // output gradient hold a non-finite value uses binary32 LDS atomic adds.
 template <int DT, int RC, int CC>
-__global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
+__global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blocks, uint32_t per_xcd)
 {
     using E = Elem<DT>;
     constexpr int s = E::kBytes;
@@ -232,7 +232,10 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
     __shared__ float red[2][16];
     __shared__ bool flag[16];
     const int chunks = a.Cg / CC;
-    const uint32_t b = blockIdx.x;
+    // renumbered so that each XCD runs a contiguous range: the groups of an
+    // image, whose rows share cache lines, meet in one L2
+    uint32_t b;
+    if (!logical_block(blockIdx.x, total_blocks, per_xcd, &b)) return;
     const uint32_t n = b / (uint32_t)(a.G * chunks);
     const uint32_t r = b - n * (uint32_t)(a.G * chunks);
     const uint32_t g = r / (uint32_t)chunks, ch = r - g * (uint32_t)chunks;
@@ -370,14 +373,16 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a)
 }
 
 template <int DT, int RC>
-void launch_bx_cc(const BArgs& a, unsigned grid, size_t lds, hipStream_t stream)
+void launch_bx_cc(const BArgs& a, unsigned total, size_t lds, hipStream_t stream)
 {
+    const uint32_t per_xcd = (total + 7) / 8;
+    const unsigned grid = per_xcd * 8;
     switch (a.cc) {
-        case 16: hipLaunchKernelGGL((k_backward_x<DT, RC, 16>), dim3(grid), dim3(1024), lds, stream, a); break;
-        case 8: hipLaunchKernelGGL((k_backward_x<DT, RC, 8>), dim3(grid), dim3(1024), lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((k_backward_x<DT, RC, 4>), dim3(grid), dim3(1024), lds, stream, a); break;
-        case 2: hipLaunchKernelGGL((k_backward_x<DT, RC, 2>), dim3(grid), dim3(1024), lds, stream, a); break;
-        default: hipLaunchKernelGGL((k_backward_x<DT, RC, 1>), dim3(grid), dim3(1024), lds, stream, a); break;
+        case 16: hipLaunchKernelGGL((k_backward_x<DT, RC, 16>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        case 8: hipLaunchKernelGGL((k_backward_x<DT, RC, 8>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        case 4: hipLaunchKernelGGL((k_backward_x<DT, RC, 4>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        case 2: hipLaunchKernelGGL((k_backward_x<DT, RC, 2>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        default: hipLaunchKernelGGL((k_backward_x<DT, RC, 1>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
     }
 }
 
