@@ -478,9 +478,22 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (goff || gmask || (gx && !a.cc)) {
+    // offset and weight gradients from an LDS copy of each (image, group)
+    // when it fits, unless x's gradient needs the atomics kernel anyway
+    int wblock = 0, wpitch = 0;
+    size_t wlds = 0;
+    const bool om_window = (goff || gmask) && (a.cc || !gx) && backward_om_window_plan(p, gout, &wblock, &wpitch, &wlds);
+    if (om_window) {
+        BArgs b = a;
+        b.gx = nullptr;
+        b.pitch = wpitch;
+        const hipError_t e = launch_backward_om_window(b, p.dtype, p.Cg * s / 16, wblock, wlds, stream);
+        if (e != hipSuccess) return e;
+    }
+    if ((!om_window && (goff || gmask)) || (gx && !a.cc)) {
         BArgs b = a;
         if (a.cc) b.gx = nullptr;          // the LDS kernel below takes x's gradient
+        if (om_window) b.goff = b.gmask = nullptr;
         const int64_t grid = ceil_div(a.units_total, 4 * (int64_t)a.units_per_wave);
         hipError_t e = hipErrorInvalidValue;
         switch (p.dtype) {

@@ -1,0 +1,264 @@
+// DCNv4 backward, offset and weight gradients with the corner reads served
+// from an LDS copy of the image (the forward's window idea applied to the
+// backward's gather).
+//
+// Gradients (the forward of jsqmd.com/news/933833, section 1, code example
+// "DCNv4核心计算流程示例", with raw weights per the same section and
+// bqwf.cn/news/1148139 section 2.1), per unit (pixel, group) and point k with
+// bilinear fractions (lx, ly), hx = 1 - lx, hy = 1 - ly, and A_q = sum over
+// the group's channels c of g_c * x[q]_c for the four corners q:
+//   dL/dm_k         = hy hx A00 + hy lx A01 + ly hx A10 + ly lx A11
+//   dL/doffset_x[k] = offset_scale * m_k * (hy (A01 - A00) + ly (A11 - A10))
+//   dL/doffset_y[k] = offset_scale * m_k * (hx (A10 - A00) + lx (A11 - A01))
+// (the per-channel expressions, summed over the channels first: four dot
+// products per point instead of three sums of bilinear expressions per
+// channel).  Points the forward skips get zero gradients.
+//
+// Work layout: one workgroup = (image n, group g); the whole zero-bordered
+// image of that group, [-1, H] x [-1, W], is copied to LDS (one plane per
+// 16-byte channel vector, rows of `pitch` entries, the columns past W + 1
+// zero), so every corner of every point is read from LDS.  One lane = one
+// (unit, point) with all of the group's channels.  Workgroups are renumbered
+// per XCD so that an image's groups, whose rows share cache lines, meet in
+// one L2.  The results are deterministic (a fixed operation order).
+
+#include "dcnv4_device.h"
+#include "dcnv4_internal.h"
+#include "dcnv4_kernels.h"
+
+namespace dcnv4 {
+namespace {
+
+// A += sum over the vector's elements e of g[e] * v_e, in element order.
+template <int DT>
+__device__ __forceinline__ float dot_vec16(float A, const float* g, u32x4 v)
+{
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (DT == DCNV4_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A = fmaf(g[i], __uint_as_float(d[i]), A);
+    } else if constexpr (DT == DCNV4_F16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2 h = __builtin_bit_cast(f16x2, d[i]);
+            A = fmaf(g[2 * i], (float)h.x, A);
+            A = fmaf(g[2 * i + 1], (float)h.y, A);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            A = fmaf(g[2 * i], bf16_lo(d[i]), A);
+            A = fmaf(g[2 * i + 1], bf16_hi(d[i]), A);
+        }
+    }
+    return A;
+}
+
+// One lane per (unit, point): the P lanes of a unit are consecutive, so the
+// unit's P values of each gradient row are written by one store instruction
+// as one contiguous piece (per-lane stores of a unit's whole row would touch
+// a different cache line in every lane).  Each lane reads its point's offset
+// pair and weight and the unit's output gradient (the same 16-byte vectors
+// for the unit's P lanes).
+template <int DT, int NV, int RC>
+__global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t total_blocks, uint32_t per_xcd)
+{
+    using E = Elem<DT>;
+    constexpr int s = E::kBytes;
+    constexpr int EPV = kPerVec<DT>;
+    constexpr int P = 9 - RC;                  // points (K = 3)
+    constexpr int UPW = 64 / P;                // units per wave (the last 64 % P lanes idle)
+    extern __shared__ u32x4 lds[];
+    const uint32_t B = blockDim.x;
+
+    uint32_t lb;
+    if (!logical_block(blockIdx.x, total_blocks, per_xcd, &lb)) return;
+    const uint32_t n = fdiv(lb, a.div_G);
+    const uint32_t g = lb - n * (uint32_t)a.G;
+
+    const char* xs = static_cast<const char*>(a.x) + (int64_t)n * a.img_x_elems * s;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs, a.img_x_bytes);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(static_cast<const char*>(a.off) + (int64_t)n * a.img_off_elems * s, a.img_off_bytes);
+    const __amdgpu_buffer_rsrc_t rm =
+        make_rsrc(static_cast<const char*>(a.msk) + (int64_t)n * a.img_mask_elems * s, a.img_mask_bytes);
+    const __amdgpu_buffer_rsrc_t rg =
+        make_rsrc(static_cast<const char*>(a.gout) + (int64_t)n * a.img_out_elems * s, a.img_out_bytes);
+    const uint32_t pix_bytes = (uint32_t)a.C * s;
+    const uint32_t row_bytes = (uint32_t)a.W * pix_bytes;
+    const uint32_t grp_bytes = g * (uint32_t)a.Cg * s;
+
+    // ---- the window: entry (plane v, row r, column c) holds image pixel
+    // (r - 1, c - 1), channels [v * EPV, v * EPV + EPV) of group g; zero off
+    // the image.  Chunk q = pixel entry q / NV, plane q % NV: consecutive
+    // lanes read consecutive 16-byte pieces of x.
+    const uint32_t pitch = (uint32_t)a.pitch;
+    const uint32_t WH = (uint32_t)a.H + 2;
+    const uint32_t plane16 = WH * pitch;
+    const uint32_t nchunks = plane16 * NV;
+    {
+        constexpr int U = 8;
+        for (uint32_t c0 = threadIdx.x; c0 < nchunks; c0 += B * U) {
+            u32x4 v[U];
+            uint32_t dst[U];
+#pragma unroll
+            for (int r = 0; r < U; ++r) {
+                const uint32_t c = c0 + r * B;
+                const uint32_t p = c / NV;
+                const uint32_t cv = c - p * NV;
+                const uint32_t wy = p / pitch, wx = p - wy * pitch;
+                const int y = (int)wy - 1, x = (int)wx - 1;
+                const bool in = (c < nchunks) & (y >= 0) & (y < a.H) & (x >= 0) & (x < a.W);
+                const uint32_t voff = (uint32_t)y * row_bytes + (uint32_t)x * pix_bytes + grp_bytes + cv * 16u;
+                v[r] = buf_load16(rx, in ? voff : kOobOffset);
+                dst[r] = cv * plane16 + p;
+            }
+#pragma unroll
+            for (int r = 0; r < U; ++r)
+                if (c0 + r * B < nchunks) lds[dst[r]] = v[r];
+        }
+    }
+    __syncthreads();
+
+    const char* lbase = reinterpret_cast<const char*>(lds);
+    const int row16 = (int)pitch * 16;
+    const int plane = (int)plane16 * 16;
+    const float fW = (float)a.W, fH = (float)a.H;
+    // a point that contributes nothing reads the zero columns W + 1, W + 2
+    const float zx = (float)(a.W + 1), zy = -1.0f;
+    const uint32_t units = (uint32_t)(a.Ho * a.Wo);
+    const float scale = a.offset_scale;
+
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t ul = lane / P;              // unit within the wave
+    const int k = (int)(lane - ul * P);        // point
+    const int q = (RC && k >= 4) ? k + 1 : k;  // grid position of the point
+    const int pi = q / 3, pj = q % 3;
+    const uint32_t upass = (B >> 6) * UPW;     // units per pass of the workgroup
+    for (uint32_t u0 = wave * UPW; u0 < units; u0 += upass) {
+        const uint32_t u = u0 + ul;
+        if (ul >= UPW || u >= units) continue;
+        const uint32_t oy = fdiv(u, a.div_Wo);
+        const uint32_t ox = u - oy * (uint32_t)a.Wo;
+        const int64_t prow = (int64_t)u * a.off_row + (int64_t)g * 2 * P;     // within the image
+        const int64_t mrow = (int64_t)u * a.mask_row + (int64_t)g * P;
+        float dx, dy, m;
+        if constexpr (s == 4) {
+            dx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (int)((prow + k) * 4), 0, 0));
+            dy = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (int)((prow + P + k) * 4), 0, 0));
+            m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, (int)((mrow + k) * 4), 0, 0));
+        } else {
+            dx = E::raw_to_f(__builtin_amdgcn_raw_buffer_load_b16(ro, (int)((prow + k) * 2), 0, 0));
+            dy = E::raw_to_f(__builtin_amdgcn_raw_buffer_load_b16(ro, (int)((prow + P + k) * 2), 0, 0));
+            m = E::raw_to_f(__builtin_amdgcn_raw_buffer_load_b16(rm, (int)((mrow + k) * 2), 0, 0));
+        }
+        u32x4 gv[NV];
+        const uint32_t go = (u * (uint32_t)a.C + g * (uint32_t)a.Cg) * s;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) gv[v] = buf_load16(rg, go + 16u * v);
+
+        float px = fmaf(dx, scale, (float)((int)ox * a.stride - a.pad + pj * a.dil));
+        float py = fmaf(dy, scale, (float)((int)oy * a.stride - a.pad + pi * a.dil));
+        const bool valid = (px > -1.0f) & (px < fW) & (py > -1.0f) & (py < fH);
+        px = valid ? px : zx;
+        py = valid ? py : zy;
+        const float fx = floorf(px), fy = floorf(py);
+        const float lx = px - fx, ly = py - fy;
+        const float hx = 1.0f - lx, hy = 1.0f - ly;
+        // window entry of corner (y0, x0): (y0 + 1, x0 + 1)
+        const int a00 = ((int)fy + 1) * row16 + (((int)fx + 1) << 4);
+        float A00 = 0.0f, A01 = 0.0f, A10 = 0.0f, A11 = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const char* p0 = lbase + a00 + v * plane;
+            const u32x4 c00 = *reinterpret_cast<const u32x4*>(p0);
+            const u32x4 c01 = *reinterpret_cast<const u32x4*>(p0 + 16);
+            const u32x4 c10 = *reinterpret_cast<const u32x4*>(p0 + row16);
+            const u32x4 c11 = *reinterpret_cast<const u32x4*>(p0 + row16 + 16);
+            float gr[EPV];
+            const uint32_t w[4] = {gv[v].x, gv[v].y, gv[v].z, gv[v].w};
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                if constexpr (s == 4) gr[e] = __uint_as_float(w[e]);
+                else gr[e] = E::raw_to_f((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+            }
+            A00 = dot_vec16<DT>(A00, gr, c00);
+            A01 = dot_vec16<DT>(A01, gr, c01);
+            A10 = dot_vec16<DT>(A10, gr, c10);
+            A11 = dot_vec16<DT>(A11, gr, c11);
+        }
+        float sm = (hy * hx) * A00;
+        sm = fmaf(hy * lx, A01, sm);
+        sm = fmaf(ly * hx, A10, sm);
+        sm = fmaf(ly * lx, A11, sm);
+        const float sx = fmaf(hy, A01 - A00, ly * (A11 - A10));
+        const float sy = fmaf(hx, A10 - A00, lx * (A11 - A01));
+        const float ms = scale * m;
+        if (a.goff) {
+            float* gop = a.goff + (int64_t)n * a.img_off_elems + prow;
+            gop[k] = valid ? ms * sx : 0.0f;
+            gop[P + k] = valid ? ms * sy : 0.0f;
+        }
+        if (a.gmask) a.gmask[(int64_t)n * a.img_mask_elems + mrow + k] = valid ? sm : 0.0f;
+    }
+}
+
+template <int DT, int NV>
+void launch_rc(const BArgs& a, int block, uint32_t total, size_t lds, hipStream_t stream)
+{
+    const uint32_t per_xcd = (total + 7) / 8;
+    if (a.remove_center)
+        hipLaunchKernelGGL((k_backward_om_window<DT, NV, 1>), dim3(per_xcd * 8), dim3(block), lds, stream, a,
+                           total, per_xcd);
+    else
+        hipLaunchKernelGGL((k_backward_om_window<DT, NV, 0>), dim3(per_xcd * 8), dim3(block), lds, stream, a,
+                           total, per_xcd);
+}
+
+template <int DT>
+hipError_t launch_nv(const BArgs& a, int nv, int block, uint32_t total, size_t lds, hipStream_t stream)
+{
+    switch (nv) {
+        case 1: launch_rc<DT, 1>(a, block, total, lds, stream); break;
+        case 2: launch_rc<DT, 2>(a, block, total, lds, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_om_window_plan(const Problem& p, const void* gout, int* block, int* pitch, size_t* lds)
+{
+    const int s = p.dtype == DCNV4_F32 ? 4 : 2;
+    if (p.K != 3 || (p.Cg * s) % 16) return false;
+    const int nv = p.Cg * s / 16;
+    if (nv > 2) return false;
+    if ((uintptr_t)p.x % 16 || (uintptr_t)gout % 16) return false;
+    // at least two zero columns past the image's right border, rows a whole
+    // number of 16-entry bank groups apart (as the forward's windows)
+    const int pt = (p.W + 2 + 2 + 15) / 16 * 16;
+    const int64_t bytes = (int64_t)(p.H + 2) * pt * nv * 16;
+    if (bytes > kLdsPerCu) return false;
+    const int64_t units = (int64_t)p.Ho * p.Wo;
+    int b = (int)((units + 63) / 64 * 64);
+    if (b > 1024) b = 1024;
+    *block = b;
+    *pitch = pt;
+    *lds = (size_t)bytes;
+    return true;
+}
+
+hipError_t launch_backward_om_window(const BArgs& a, int dtype, int nv, int block, size_t lds,
+                                     hipStream_t stream)
+{
+    const uint32_t total = (uint32_t)(a.units_total / a.units_img) * (uint32_t)a.G;   // images x groups
+    switch (dtype) {
+        case DCNV4_F32: return launch_nv<DCNV4_F32>(a, nv, block, total, lds, stream);
+        case DCNV4_F16: return launch_nv<DCNV4_F16>(a, nv, block, total, lds, stream);
+        case DCNV4_BF16: return launch_nv<DCNV4_BF16>(a, nv, block, total, lds, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dcnv4

@@ -56,6 +56,11 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
 int backward_vec_bytes(const Problem& p, const void* gout);
 // Channels per workgroup of the LDS x-gradient kernel (0: global atomics instead).
 int backward_x_chunk(const Problem& p);
+// Whether the offset/weight gradients can read their corners from an LDS copy
+// of each (image, group) (K = 3, one or two 16-byte vectors per unit, 16-byte
+// aligned x and output gradient, the bordered image within the LDS), and
+// that kernel's workgroup size, window row pitch and LDS bytes.
+bool backward_om_window_plan(const Problem& p, const void* gout, int* block, int* pitch, size_t* lds);
 hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
                            hipStream_t stream);
 

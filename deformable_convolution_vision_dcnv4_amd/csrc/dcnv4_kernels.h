@@ -92,12 +92,18 @@ struct BArgs {
     int units_per_wave;
     int cc;                         // x-gradient LDS kernel: channels per workgroup (0 = atomics path)
     int cbits;                      // x-gradient LDS kernel: log2 bound of the terms per element
+    int pitch;                      // offset/weight-gradient LDS kernel: window row pitch (16-byte entries)
     uint32_t units_img;
     int64_t units_total;
     FastDiv div_units_img, div_G, div_Wo;
 };
 
 hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hipStream_t stream);
+// Offset/weight gradients with the image of each (image, group) in LDS:
+// N * G workgroups of `block` threads, `lds` bytes of window, 16-byte
+// vectors per unit nv (1 or 2).
+hipError_t launch_backward_om_window(const BArgs& a, int dtype, int nv, int block, size_t lds,
+                                     hipStream_t stream);
 hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);
 
 // Window kernel limits the planner needs: threads per workgroup it is
