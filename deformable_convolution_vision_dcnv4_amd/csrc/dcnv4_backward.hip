@@ -215,8 +215,8 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a, uint32_t total_blocks
 //
 // The accumulation is in 64-bit fixed point with LDS integer atomic adds
 // (binary32 LDS atomic adds run tens of times slower on this GPU).  Each
-// term t = w * g (binary32, as the float path computes it) becomes
-// rint(t * 2^F); F is fixed per (image, group) so that no sum can overflow:
+// term w * g (the exact product of the binary32 factors) becomes
+// rint(w * g * 2^F); F is fixed per (image, group) so that no sum can overflow:
 // with M = max|m| * max|g| over the (image, group) (|t| <= M) and at most
 // 2^cbits terms per element, F = 62 - cbits - e where M < 2^e.  Integer sums
 // do not depend on the order of the adds, so x's gradient is reproducible;
@@ -302,6 +302,7 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
         F = 62 - a.cbits - e;
     }
 
+    const double scaleF = ldexp(1.0, F);
     const float fW = (float)a.W, fH = (float)a.H;
     float* accf = reinterpret_cast<float*>(acc);
     for (int pix = threadIdx.x; pix < npix; pix += blockDim.x) {
@@ -314,8 +315,12 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
         mrow.load(rm, (uint32_t)(((int64_t)pix * a.mask_row + (int64_t)g * P) * s));
         grow.load(rg, (uint32_t)(((int64_t)pix * a.C + (int64_t)g * a.Cg + (int64_t)ch * CC) * s));
         float gr[CC];
+        double gd[CC];
 #pragma unroll
-        for (int c = 0; c < CC; ++c) gr[c] = grow.get(c);
+        for (int c = 0; c < CC; ++c) {
+            gr[c] = grow.get(c);
+            gd[c] = (double)gr[c];
+        }
         const int bx0 = wo * a.stride - a.pad, by0 = ho * a.stride - a.pad;
 #pragma unroll
         for (int k = 0; k < P; ++k) {
@@ -334,27 +339,31 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
             const int cell[4] = {0, 1, WP, WP + 1};
             // corner (y0, x0) of the bordered image; the others follow
             const int c00 = (y0 + 1) * WP + (x0 + 1);
+            if (fixed) {
+                // term w * g on the grid of 2^-F: the product of the binary32
+                // factors is exact in binary64 (w pre-scaled by 2^F, exactly),
+                // rounded to an integer q, |q| < 2^62; q = hi * 2^32 + lo with
+                // lo in [0, 2^32) is its two's-complement 64-bit pattern
+                double wd[4];
 #pragma unroll
-            for (int cr = 0; cr < 4; ++cr) {
+                for (int cr = 0; cr < 4; ++cr) wd[cr] = (double)w[cr] * scaleF;
 #pragma unroll
-                for (int c = 0; c < CC; ++c) {
-                    const float t = w[cr] * gr[c];
-                    const int idx = c * plane + c00 + cell[cr];
-                    if (fixed) {
-                        // rint(t * 2^F) as a two's-complement 64-bit integer, from the
-                        // magnitude's high and low 32-bit parts (both exact in binary32:
-                        // below 2^32 the magnitude is an integer < 2^32, above it a
-                        // multiple of 2^9)
-                        const float qf = rintf(ldexpf(t, F));
-                        const float mag = fabsf(qf);
-                        const float hi = floorf(mag * 0x1p-32f);
-                        const float lo = mag - hi * 0x1p32f;
+                for (int cr = 0; cr < 4; ++cr) {
+#pragma unroll
+                    for (int c = 0; c < CC; ++c) {
+                        const double q = rint(wd[cr] * gd[c]);
+                        const double hi = floor(q * 0x1p-32);
+                        const double lo = fma(-hi, 0x1p32, q);
                         const unsigned long long u =
-                            ((unsigned long long)(uint32_t)hi << 32) + (unsigned long long)(uint32_t)lo;
-                        atomicAdd(&acc[idx], qf < 0.0f ? 0ull - u : u);
-                    } else {
-                        atomicAdd(&accf[idx], t);
+                            ((unsigned long long)(uint32_t)(int32_t)hi << 32) + (unsigned long long)(uint32_t)lo;
+                        atomicAdd(&acc[c * plane + c00 + cell[cr]], u);
                     }
+                }
+            } else {
+#pragma unroll
+                for (int cr = 0; cr < 4; ++cr) {
+#pragma unroll
+                    for (int c = 0; c < CC; ++c) atomicAdd(&accf[c * plane + c00 + cell[cr]], w[cr] * gr[c]);
                 }
             }
         }
