@@ -147,7 +147,8 @@ int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, v
  * Any gradient pointer may be NULL (not computed).  Arithmetic is binary32;
  * grad_offset and grad_mask are summed in a fixed order (reproducible).
  * grad_x: for K = 3 when a few channels of the zero-bordered image fit in
- * LDS, each term w*g is rounded to a multiple of 2^-F and summed exactly in
+ * LDS, each term w*g (the exact product of its binary32 factors) is rounded
+ * to a multiple of 2^-F and summed exactly in
  * 64-bit integers (reproducible; F per (image, group) from the largest
  * |weight| * |grad_out| and the term count, so sums cannot overflow; the
  * binary32 path if either holds a non-finite value); otherwise summed with
