@@ -39,6 +39,7 @@ struct Plan {
     int coal;       // window: offset rows staged through LDS per wave
     int lds_bytes;  // dynamic LDS (window)
     int lds_total;  // all LDS per workgroup (the coalesced variant adds static buffers)
+    int lpu;        // window: lanes per unit (> 1: one 16-byte vector per lane)
 };
 
 // Largest LDS allocation one workgroup may use on gfx950 (the CU's 160 KiB).

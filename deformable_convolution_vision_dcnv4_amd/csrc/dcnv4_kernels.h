@@ -69,6 +69,9 @@ struct KArgs {
     FastDiv div_GB, div_TW, div_tiles_x, div_tiles_y, div_gtiles, div_CPS, div_pitch;
     uint32_t win_bytes;             // LDS of the window (the per-wave offset buffers follow)
     uint32_t lds_bytes;             // all dynamic LDS
+    int lpu;                        // lanes per unit (> 1: one 16-byte vector per lane)
+    int nvt;                        // 16-byte vectors per unit
+    FastDiv div_lpu;
 };
 
 // Backward kernel arguments (elements of the I/O type unless named *_bytes;

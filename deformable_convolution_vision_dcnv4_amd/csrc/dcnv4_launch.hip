@@ -13,14 +13,17 @@
 //       measured fastest wherever it fits;
 //     - else bands of full-width output rows with a margin of R rows for the
 //       offsets (R = 5 unless tuned), for the smallest GB, when at most four
-//       bands cover the image: band height chosen to minimise (rounds of
-//       workgroups) x (rows computed + rows staged / 2).  With more bands the
-//       margins cost more staging than LDS saves, and large offsets (whose
-//       units fall back to global reads) make it worse;
-//   threads per workgroup: the kernel's maximum, or fewer when one pass covers
-//   the tile.  The direct family otherwise.
+//       bands (eight for units of three or more vectors) cover the image:
+//       band height chosen to minimise (rounds of workgroups) x (rows
+//       computed + rows staged / 2).  With more bands the margins cost more
+//       staging than LDS saves, and large offsets (whose units fall back to
+//       global reads) make it worse;
+//   units of three or more 16-byte vectors take one lane per vector (measured
+//   8-15% faster than whole-unit lanes, which cap a workgroup at 512
+//   threads); threads per workgroup: the kernel's maximum, or fewer when one
+//   pass covers the tile.  The direct family otherwise.
 // DCNV4_TUNE (environment, read once) overrides the choices for tuning runs:
-// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1,pitch_add=E,coal=0|1".
+// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1,pitch_add=E,coal=0|1,split=0|1".
 
 #include <stdio.h>
 #include <stdlib.h>
@@ -37,7 +40,7 @@ namespace {
 
 struct Tune {
     int kernel = 0;     // 0 auto, 1 direct, 2 window
-    int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1, pitch_add = 0, coal = -1;
+    int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1, pitch_add = 0, coal = -1, split = -1;
 };
 
 const Tune& tune()
@@ -64,6 +67,7 @@ const Tune& tune()
             else if (!strcmp(tok, "full")) t.full = atoi(v);
             else if (!strcmp(tok, "pitch_add")) t.pitch_add = atoi(v);
             else if (!strcmp(tok, "coal")) t.coal = atoi(v);
+            else if (!strcmp(tok, "split")) t.split = atoi(v);
         }
     });
     return t;
@@ -112,6 +116,9 @@ bool plan_window(const Problem& p, Plan* pl)
     if ((uintptr_t)p.x % 16 || (uintptr_t)p.out % 16) return false;
     const int ub = p.Cg * s;                   // bytes of one group of one pixel
     const int R = t.r >= 0 ? t.r : 5;          // margin for the offsets, pixels
+    // units of three or more vectors: one lane per vector (whole-unit lanes
+    // need so many registers that a workgroup is capped at 512 threads)
+    const int lpu = (t.split == 1 && nv > 1) || (t.split < 0 && nv >= 3) ? nv : 1;
     const int cus = 256;
 
     // group blocks to try, smallest first (all divisors of G unless tuned)
@@ -143,7 +150,7 @@ bool plan_window(const Problem& p, Plan* pl)
         if (t.th) max_th = t.th;
         if (max_th < 1) continue;
         const int nb0 = (int)ceil_div(p.Ho, max_th);
-        if (nb0 > 4 && !t.th) continue;
+        if (nb0 > (lpu > 1 ? 8 : 4) && !t.th) continue;
         // band count: fewest rounds of workgroups x (rows computed + half the rows staged)
         double best = 1e30;
         for (int nb = nb0; nb <= 2 * nb0; ++nb) {
@@ -166,16 +173,17 @@ bool plan_window(const Problem& p, Plan* pl)
     const int lds = lds_for(WH, WW, slot);
     if (lds > kLdsPerCu) return false;
     const int64_t units = (int64_t)TH * TW * GB;
-    const int max_block = window_max_block(nv);
-    int block = t.block ? t.block : pick_block(units, max_block);
+    const int64_t items = units * lpu;
+    const int max_block = lpu > 1 ? 1024 : window_max_block(nv);
+    int block = t.block ? t.block : pick_block(items, max_block);
     if (block < 64 || block % 64 || block > max_block) block = max_block;
-    if (ceil_div(units, block) > 64) return false;   // the kernel tracks at most 64 passes
+    if (ceil_div(items, block) > 64) return false;   // the kernel tracks at most 64 passes
 
     // offset rows through LDS: needs evenly spaced rows of one group (GB = 1,
     // full-width tiles, rows a whole number of dwords apart) and room for the
     // per-wave buffers
     const int s_el = elem_bytes(p.dtype);
-    const bool coal_ok = GB == 1 && TW == p.Wo && (p.off_row * s_el) % 4 == 0 &&
+    const bool coal_ok = lpu == 1 && GB == 1 && TW == p.Wo && (p.off_row * s_el) % 4 == 0 &&
                          p.off_row * s_el < (1 << 24) &&
                          lds + window_coal_lds_bytes(block, p.dtype, p.P) <= kLdsPerCu;
     pl->coal = t.coal == 0 ? 0 : coal_ok ? 1 : 0;
@@ -183,7 +191,8 @@ bool plan_window(const Problem& p, Plan* pl)
 
     pl->kernel = kKernelWindow;
     pl->vec = 16;
-    pl->lanes = 1;
+    pl->lanes = lpu;
+    pl->lpu = lpu;
     pl->block = block;
     pl->nv = nv;
     pl->GB = GB; pl->TH = TH; pl->TW = TW; pl->RY = full ? 0 : R; pl->RX = full ? 0 : R;
@@ -212,6 +221,7 @@ void plan_direct(const Problem& p, Plan* pl)
     pl->coal = 0;
     pl->lds_total = 0;
     pl->lds_bytes = 0;
+    pl->lpu = 1;
     const int64_t lanes_img = (int64_t)p.Ho * p.Wo * p.G * pl->lanes;
     pl->grid = (int64_t)p.N * ceil_div(lanes_img, 256);
 }
@@ -275,6 +285,9 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
     a.div_pitch = make_fastdiv((uint32_t)a.pitch);
     a.win_bytes = (uint32_t)plan.lds_bytes;
     a.lds_bytes = (uint32_t)plan.lds_total;
+    a.lpu = plan.lpu;
+    a.nvt = plan.nv;
+    a.div_lpu = make_fastdiv((uint32_t)plan.lpu);
     return launch_window(a, p.dtype, plan.nv, plan.block, plan.grid, stream);
 }
 

@@ -123,7 +123,8 @@ struct WinCtx {
     float wx_lo, wx_hi, wy_lo, wy_hi;   // window test: wx_lo <= px < wx_hi, wy_lo <= py < wy_hi
     float zx, zy;                       // position of the zero columns (top-left corner)
     int zxi, zyi;                       // the same as integers
-    int row16;                          // bytes per LDS row (pitch * 16)
+    int row16;                          // bytes per LDS row
+    int xstep;                          // bytes between horizontally adjacent pixels
     int plane;                          // bytes per LDS plane
     int cbase;                          // LDS byte of image pixel (0,0) in plane 0
     uint32_t row_bytes, pix_bytes;      // global x strides
@@ -135,7 +136,7 @@ struct WinCtx {
 // columns with weight 0.  A valid point whose corners leave a partial window
 // reads the zero columns too and sets `fb`: its whole unit is then
 // recomputed from global memory by unit_global (same operation order).
-template <int DT, int NV, int FULL, int RC, int P>
+template <int DT, int NV, int FULL, int RC, int P, int SPLIT>
 __device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
                                                      const RowLoad<DT, P>& msk, int k, int bx, int by,
                                                      int ubase, bool& fb)
@@ -168,16 +169,17 @@ __device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowL
     r.w01 = mhy * lx;
     r.w10 = mly * hx;
     r.w11 = mly * lx;
-    const int a00 = __mul24(y0, x.row16) + (x0 << 4) + ubase;
+    const int a00 = __mul24(y0, x.row16) + (SPLIT ? __mul24(x0, x.xstep) : (x0 << 4)) + ubase;
     const int a10 = a00 + x.row16;
+    const int step01 = SPLIT ? x.xstep : 16;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const char* p0 = x.lbase + a00 + v * x.plane;
         const char* p1 = x.lbase + a10 + v * x.plane;
         r.v00[v] = *reinterpret_cast<const u32x4*>(p0);
-        r.v01[v] = *reinterpret_cast<const u32x4*>(p0 + 16);
+        r.v01[v] = *reinterpret_cast<const u32x4*>(p0 + step01);
         r.v10[v] = *reinterpret_cast<const u32x4*>(p1);
-        r.v11[v] = *reinterpret_cast<const u32x4*>(p1 + 16);
+        r.v11[v] = *reinterpret_cast<const u32x4*>(p1 + step01);
     }
     return r;
 }
@@ -252,14 +254,20 @@ __device__ __forceinline__ void unit_global(float* acc, const WinCtx& x, const R
     }
 }
 
-template <int DT, int NV, int FULL, int RC, int COAL, int MAXB>
+// SPLIT (with NV = 1, no coalesced rows): a.lpu consecutive lanes share a
+// unit, lane v of them taking 16-byte vector v of the unit's channels (for
+// units of many vectors, whose whole-unit registers would cap a workgroup at
+// 512 threads).  The window then holds each pixel's vectors side by side,
+// (row, column, vector), so that a unit's lanes read neighbouring entries.
+template <int DT, int NV, int FULL, int RC, int COAL, int SPLIT, int MAXB>
 __global__ void __launch_bounds__(MAXB)
 k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 {
+    static_assert(!SPLIT || (NV == 1 && !COAL), "split units: one vector per lane, per-lane rows");
     using E = Elem<DT>;
     constexpr int s = E::kBytes;
     constexpr int EPV = kPerVec<DT>;          // elements per 16-byte vector
-    constexpr int NC = NV * EPV;              // channels per unit (= Cg)
+    constexpr int NC = NV * EPV;              // channels per lane (= Cg unless SPLIT)
     constexpr int P = 9 - RC;                 // points (K = 3)
     constexpr int ND = 2 * P * s / 4;         // dwords of one unit's offset row
     extern __shared__ u32x4 lds[];
@@ -297,6 +305,10 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(os_img, a.img_off_bytes);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(ms_img, a.img_mask_bytes);
     const uint32_t units = (uint32_t)(a.TH * a.TW * a.GB);
+    // lanes' work items: units, or (unit, vector) pairs when SPLIT
+    const uint32_t lpu = SPLIT ? (uint32_t)a.lpu : 1u;
+    const uint32_t items = units * lpu;
+    auto unit_of_item = [&](uint32_t it) { return SPLIT ? fdiv(it, a.div_lpu) : it; };
 
     // unit u of this workgroup -> (pixel, group); its offset/weight rows are
     // prefetched one unit ahead
@@ -344,9 +356,9 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             stage_offset_rows<ND>(os_img, a.img_off_bytes, wbuf, lane,
                                   off_tile_base + (threadIdx.x - lane) * off_row_bytes, off_row_bytes);
             if (threadIdx.x < units) msk.issue(rm, lin_sm);
-        } else if (threadIdx.x < units) {
+        } else if (threadIdx.x < items) {
             int oy, ox, gl;
-            unit_of(threadIdx.x, oy, ox, gl);
+            unit_of(unit_of_item(threadIdx.x), oy, ox, gl);
             uint32_t so, sm;
             row_starts(min(oy, a.Ho - 1), min(ox, a.Wo - 1), gl, so, sm);
             offs.issue(ro, so);
@@ -355,10 +367,11 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     };
 
     // ---- stage the window.  Chunk c = (window pixel p = c / CPS, chunk
-    // cc = c % CPS of its GB*NV 16-byte chunks), read in that order (pixel-
-    // contiguous in x) and written to plane cc at (row, col) of p.  Columns
-    // from WW to the pitch stay zero, as does everything outside the image.
-    const uint32_t CPS = (uint32_t)a.GB * NV;
+    // cc = c % CPS of its CPS 16-byte chunks), read in that order (pixel-
+    // contiguous in x) and written to plane cc at (row, col) of p (SPLIT:
+    // to entry c).  Columns from WW to the pitch stay zero, as does
+    // everything outside the image.
+    const uint32_t CPS = (uint32_t)a.GB * (SPLIT ? (uint32_t)a.nvt : (uint32_t)NV);
     const uint32_t pitch = (uint32_t)a.pitch;
     const uint32_t plane16 = (uint32_t)a.WH * pitch;          // entries per plane
     const uint32_t nchunks = plane16 * CPS;
@@ -382,7 +395,7 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
                 const uint32_t voff = (uint32_t)y * row_bytes + (uint32_t)x * pix_bytes + grp_bytes + cc * 16u;
                 const uint32_t o = in ? voff : kOobOffset;
                 v[r] = buf_load16(rx, o);
-                dst[r] = cc * plane16 + p;
+                dst[r] = SPLIT ? c : cc * plane16 + p;
             }
             if (!rows_issued) {
                 fence_sched();
@@ -419,9 +432,10 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     cx.zyi = wy0;
     cx.zx = (float)cx.zxi;
     cx.zy = (float)cx.zyi;
-    cx.row16 = (int)pitch * 16;
-    cx.plane = (int)plane16 * 16;
-    cx.cbase = -(wy0 * (int)pitch + wx0) * 16;
+    cx.xstep = SPLIT ? (int)CPS * 16 : 16;
+    cx.row16 = (int)pitch * cx.xstep;
+    cx.plane = SPLIT ? 16 : (int)plane16 * 16;
+    cx.cbase = -(wy0 * (int)pitch + wx0) * cx.xstep;
     cx.row_bytes = row_bytes;
     cx.pix_bytes = pix_bytes;
     cx.H = a.H;
@@ -444,8 +458,10 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         if (COAL) {
             oy = lin_oy; ox = lin_ox; gl = 0;
         } else {
-            unit_of(u, oy, ox, gl);
+            unit_of(unit_of_item(u), oy, ox, gl);
         }
+        // SPLIT: this lane's vector of the unit
+        const uint32_t vsub = SPLIT ? u - unit_of_item(u) * lpu : 0u;
         RowLoad<DT, 2 * P> co = offs;
         if (!COAL) co.finish();
         if (COAL) {
@@ -476,7 +492,7 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         // computes (without a per-lane test in the coalesced variant: rows
         // past the image read as zeros and are never used)
         uint32_t nso = 0, nsm = 0;
-        const bool more = u + B < units;
+        const bool more = u + B < items;
         if (COAL && NEXT)
             stage_offset_rows<ND>(os_img, a.img_off_bytes, wbuf, lane, off_tile_base + (u - lane + B) * off_row_bytes,
                                   off_row_bytes);
@@ -492,7 +508,7 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             if (lin_ox >= a.Wo) { lin_ox -= a.Wo; ++lin_oy; }
         } else if (NEXT && more) {
             int oy2, ox2, gl2;
-            unit_of(u + B, oy2, ox2, gl2);
+            unit_of(unit_of_item(u + B), oy2, ox2, gl2);
             row_starts(min(oy2, a.Ho - 1), min(ox2, a.Wo - 1), gl2, nso, nsm);
             offs.issue(ro, nso);
             msk.issue(rm, nsm);
@@ -507,15 +523,15 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 
         const int bx = __mul24(ox, a.stride) - a.pad;
         const int by = __mul24(oy, a.stride) - a.pad;
-        const int ubase = gl * NV * cx.plane + cx.cbase;
+        const int ubase = SPLIT ? (int)((gl * a.nvt + vsub) * 16u) + cx.cbase : gl * NV * cx.plane + cx.cbase;
 
         // two points in flight: issue the reads of point k+1, then accumulate point k
         bool fb = false;
-        PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P>(cx, co, cm, 0, bx, by, ubase, fb);
+        PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, cm, 0, bx, by, ubase, fb);
 #pragma unroll
         for (int k = 0; k < P; ++k) {
             PointRegs<NV> nxt;
-            if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P>(cx, co, cm, k + 1, bx, by, ubase, fb);
+            if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, cm, k + 1, bx, by, ubase, fb);
             fence_sched();
             pin(cur);
             consume_point<DT, NV>(acc, cur);
@@ -533,7 +549,8 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             op = static_cast<char*>(a.out) + (int64_t)n * a.img_out_elems * s + oo;
         } else {
             const int64_t pix = (int64_t)oy * a.Wo + ox;
-            op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s;
+            op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s +
+                 vsub * 16u;
         }
 #pragma unroll
         for (int v = 0; v < NV; ++v)
@@ -546,7 +563,7 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         if (u < units) unit_pass(std::false_type{}, pass);
     } else {
         // (per-lane requests of the next unit's rows, see `more`)
-        for (; u < units; u += B, ++pass) unit_pass(std::true_type{}, pass);
+        for (; u < items; u += B, ++pass) unit_pass(std::true_type{}, pass);
     }
 
     if (!FULL) {
@@ -554,7 +571,9 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             const uint32_t pass = (uint32_t)__builtin_ctzll(fbmask);
             fbmask &= fbmask - 1;
             int oy, ox, gl;
-            unit_of(threadIdx.x + pass * B, oy, ox, gl);
+            const uint32_t it = threadIdx.x + pass * B;
+            unit_of(unit_of_item(it), oy, ox, gl);
+            const uint32_t vb = SPLIT ? (it - unit_of_item(it) * lpu) * 16u : 0u;   // this lane's vector
             const int g = g0 + gl;
             uint32_t so, sm;
             row_starts(oy, ox, gl, so, sm);
@@ -564,9 +583,9 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             fm.load(rm, sm);
             float acc[NC];
             unit_global<DT, NV, RC, P>(acc, cx, fo, fm, ox * a.stride - a.pad, oy * a.stride - a.pad,
-                                       (uint32_t)(g * a.Cg) * s);
+                                       (uint32_t)(g * a.Cg) * s + vb);
             const int64_t pix = (int64_t)oy * a.Wo + ox;
-            char* op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s;
+            char* op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s + vb;
 #pragma unroll
             for (int v = 0; v < NV; ++v)
                 *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
@@ -587,13 +606,13 @@ namespace {
 
 template <int NV> constexpr int kMaxBlock = NV <= 2 ? 1024 : 512;
 
-template <int DT, int NV, int FULL, int RC, int COAL>
+template <int DT, int NV, int FULL, int RC, int COAL, int SPLIT = 0>
 hipError_t launch5(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
     if (block > kMaxBlock<NV> || block < 64 || block % 64) return hipErrorInvalidValue;
     const uint32_t total = (uint32_t)grid;
     const uint32_t per_xcd = (total + 7) / 8;
-    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, COAL, kMaxBlock<NV>>), dim3(per_xcd * 8), dim3(block),
+    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, COAL, SPLIT, kMaxBlock<NV>>), dim3(per_xcd * 8), dim3(block),
                        a.lds_bytes, stream, a, total, per_xcd);
     return hipGetLastError();
 }
@@ -603,6 +622,18 @@ hipError_t launch4(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
     return a.coal ? launch5<DT, NV, FULL, RC, 1>(a, block, grid, stream)
                   : launch5<DT, NV, FULL, RC, 0>(a, block, grid, stream);
+}
+
+// Units split over a.lpu lanes, one 16-byte vector each.
+template <int DT>
+hipError_t launch_split(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+{
+    if (a.coal || a.lpu < 2) return hipErrorInvalidValue;
+    if (a.full)
+        return a.remove_center ? launch5<DT, 1, 1, 1, 0, 1>(a, block, grid, stream)
+                               : launch5<DT, 1, 1, 0, 0, 1>(a, block, grid, stream);
+    return a.remove_center ? launch5<DT, 1, 0, 1, 0, 1>(a, block, grid, stream)
+                           : launch5<DT, 1, 0, 0, 0, 1>(a, block, grid, stream);
 }
 
 template <int DT, int NV>
@@ -618,6 +649,7 @@ hipError_t launch_nv(const KArgs& a, int block, int64_t grid, hipStream_t stream
 template <int DT>
 hipError_t launch_dt(const KArgs& a, int nv, int block, int64_t grid, hipStream_t stream)
 {
+    if (a.lpu > 1) return launch_split<DT>(a, block, grid, stream);
     switch (nv) {
         case 1: return launch_nv<DT, 1>(a, block, grid, stream);
         case 2: return launch_nv<DT, 2>(a, block, grid, stream);

@@ -114,7 +114,8 @@ def test_plan_kernel_family_and_read_width(dtype, Cg, xoff, K, kernel, vec):
     if kernel == "direct":
         assert pl.lanes_per_unit * pl.vec == Cg * s
     else:
-        assert pl.lanes_per_unit == 1 and pl.lds_bytes <= 160 * 1024
+        # one lane per unit, or (units of three or more 16-byte vectors) one per vector
+        assert pl.lanes_per_unit in (1, Cg * s // 16) and pl.lds_bytes <= 160 * 1024
         assert pl.window_h >= pl.tile_h + 2 and pl.window_w >= pl.tile_w + 2
 
 

@@ -40,9 +40,15 @@ def gkw(wl):
                 offset_scale=wl.offset_scale, remove_center=wl.remove_center)
 
 
-# (name, N, H, W, G, Cg, offset std, dtypes, expected kernel family, full window)
+# (name, N, H, W, G, Cg, offset std, dtypes, expected kernel family, full
+# window).  Units of three or more 16-byte vectors (fp32 Cg=16, 16-bit
+# Cg=24/32/40) take one lane per vector; window_gb holds several groups per
+# workgroup.
 PATHS = [
     ("window_full", 2, 12, 13, 4, 16, 2.0, ("f32", "f16", "bf16"), "window", 1),
+    ("window_gb", 2, 6, 7, 4, 16, 2.0, ("f32", "bf16"), "window", 1),
+    ("window_full40", 2, 20, 22, 2, 40, 2.0, ("f16", "bf16"), "window", 1),
+    ("window_bands24", 2, 60, 60, 1, 24, 6.0, ("f16",), "window", 0),
     ("window_bands", 2, 60, 60, 1, 16, 8.0, ("f32",), "window", 0),
     ("window_bands16", 2, 60, 60, 2, 32, 6.0, ("f16", "bf16"), "window", 0),
     ("direct", 2, 12, 13, 4, 6, 2.0, ("f32", "f16", "bf16"), "direct", 0),
