@@ -218,7 +218,8 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a, uint32_t total_blocks
 // term w * g (the exact product of the binary32 factors) becomes
 // rint(w * g * 2^F); F is fixed per (image, group) so that no sum can overflow:
 // with M = max|m| * max|g| over the (image, group) (|t| <= M) and at most
-// 2^cbits terms per element, F = 62 - cbits - e where M < 2^e.  Integer sums
+// 2^cbits terms per element, F = 62 - cbits - e where M < 2^e (at most
+// 51 - e, which keeps every term below 2^51).  Integer sums
 // do not depend on the order of the adds, so x's gradient is reproducible;
 // each term is off by at most 2^-(F+1).  An (image, group) whose weights or
 // output gradient hold a non-finite value uses binary32 LDS atomic adds.
@@ -299,7 +300,8 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
     if (fixed && M > 0.0f) {
         int e;
         frexpf(M, &e);                        // M < 2^e
-        F = 62 - a.cbits - e;
+        // sums below 2^62, and each term below 2^51 (for the conversion below)
+        F = (a.cbits < 11 ? 51 : 62 - a.cbits) - e;
     }
 
     const double scaleF = ldexp(1.0, F);
@@ -342,8 +344,13 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
             if (fixed) {
                 // term w * g on the grid of 2^-F: the product of the binary32
                 // factors is exact in binary64 (w pre-scaled by 2^F, exactly),
-                // rounded to an integer q, |q| < 2^62; q = hi * 2^32 + lo with
-                // lo in [0, 2^32) is its two's-complement 64-bit pattern
+                // |product| < 2^51.  Adding 1.5 * 2^52 rounds it to the
+                // nearest integer q (ties to even) and leaves q + 2^51 in the
+                // low 52 bits of the sum's pattern, whose high 12 bits are
+                // those of 1.5 * 2^52: the pattern minus that of 1.5 * 2^52
+                // is q as a two's-complement 64-bit integer
+                constexpr double kMagic = 0x1.8p52;
+                constexpr unsigned long long kMagicBits = 0x4338000000000000ull;
                 double wd[4];
 #pragma unroll
                 for (int cr = 0; cr < 4; ++cr) wd[cr] = (double)w[cr] * scaleF;
@@ -351,11 +358,8 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
                 for (int cr = 0; cr < 4; ++cr) {
 #pragma unroll
                     for (int c = 0; c < CC; ++c) {
-                        const double q = rint(wd[cr] * gd[c]);
-                        const double hi = floor(q * 0x1p-32);
-                        const double lo = fma(-hi, 0x1p32, q);
-                        const unsigned long long u =
-                            ((unsigned long long)(uint32_t)(int32_t)hi << 32) + (unsigned long long)(uint32_t)lo;
+                        const double t = wd[cr] * gd[c] + kMagic;
+                        const unsigned long long u = __double_as_longlong(t) - kMagicBits;
                         atomicAdd(&acc[c * plane + c00 + cell[cr]], u);
                     }
                 }
