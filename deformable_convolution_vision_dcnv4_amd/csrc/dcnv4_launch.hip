@@ -18,6 +18,8 @@
 //       computed + rows staged / 2).  With more bands the margins cost more
 //       staging than LDS saves, and large offsets (whose units fall back to
 //       global reads) make it worse;
+//     - else tiles of 16 x 64 outputs with a margin of 12 pixels (units of
+//       two or more vectors, one lane per vector);
 //   units of three or more 16-byte vectors take one lane per vector (measured
 //   8-15% faster than whole-unit lanes, which cap a workgroup at 512
 //   threads); threads per workgroup: the kernel's maximum, or fewer when one
@@ -115,10 +117,10 @@ bool plan_window(const Problem& p, Plan* pl)
     if (nv < 1 || nv > 5) return false;
     if ((uintptr_t)p.x % 16 || (uintptr_t)p.out % 16) return false;
     const int ub = p.Cg * s;                   // bytes of one group of one pixel
-    const int R = t.r >= 0 ? t.r : 5;          // margin for the offsets, pixels
+    int R = t.r >= 0 ? t.r : 5;                // margin for the offsets, pixels
     // units of three or more vectors: one lane per vector (whole-unit lanes
     // need so many registers that a workgroup is capped at 512 threads)
-    const int lpu = (t.split == 1 && nv > 1) || (t.split < 0 && nv >= 3) ? nv : 1;
+    int lpu = (t.split == 1 && nv > 1) || (t.split < 0 && nv >= 3) ? nv : 1;
     const int cus = 256;
 
     // group blocks to try, smallest first (all divisors of G unless tuned)
@@ -161,6 +163,22 @@ bool plan_window(const Problem& p, Plan* pl)
             if (cost < best) { best = cost; TH = th; }
         }
         GB = gb; TW = t.tw ? t.tw : p.Wo;
+    }
+    // tiles of 16 x 64 outputs with a 12-pixel margin, one lane per vector,
+    // when rows are too wide for bands (the 256x256 shape: 11% faster than
+    // the direct kernel with its 8-pixel offsets; smaller offsets fall back
+    // less)
+    if (!GB && t.full != 1 && nv >= 2) {
+        const int R2 = t.r >= 0 ? t.r : 12;
+        const int th = t.th ? t.th : 16, tw = t.tw ? t.tw : 64;
+        for (int oi = 0; oi < no && !GB; ++oi) {
+            const int gb = order[oi];
+            if (lds_for(window_extent(th, p.stride, p.K, p.dil, R2, p.H),
+                        window_extent(tw, p.stride, p.K, p.dil, R2, p.W), gb * ub) > kLdsPerCu)
+                continue;
+            GB = gb; TH = th; TW = tw; R = R2;
+            if (t.split != 0) lpu = nv;
+        }
     }
     if (!GB) return false;
     if (!full) {

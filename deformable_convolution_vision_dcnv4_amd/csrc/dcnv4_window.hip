@@ -235,8 +235,7 @@ __device__ __forceinline__ PointRegs<NV> issue_global(const WinCtx& x, const Row
 
 // The whole unit again, every corner read from global memory: the path for
 // units with a point outside a partial window.  Same operation order as the
-// fast path, so the result is the same sequence.  One point at a time: it is
-// rare, and a lean body keeps it from taxing the fast path's registers.
+// fast path, so the result is the same sequence.
 template <int DT, int NV, int RC, int P>
 __device__ __forceinline__ void unit_global(float* acc, const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
                                             const RowLoad<DT, P>& msk, int bx, int by, uint32_t gchan)
@@ -244,13 +243,18 @@ __device__ __forceinline__ void unit_global(float* acc, const WinCtx& x, const R
     constexpr int NC = NV * kPerVec<DT>;
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
+    // two points in flight, as in the main loop (the global reads' latency
+    // would otherwise be paid once per point)
+    PointRegs<NV> cur = issue_global<DT, NV, RC, P>(x, offs, msk, 0, bx, by, gchan);
 #pragma unroll
     for (int k = 0; k < P; ++k) {
-        PointRegs<NV> r = issue_global<DT, NV, RC, P>(x, offs, msk, k, bx, by, gchan);
+        PointRegs<NV> nxt;
+        if (k + 1 < P) nxt = issue_global<DT, NV, RC, P>(x, offs, msk, k + 1, bx, by, gchan);
         fence_sched();
-        pin(r);
-        consume_point<DT, NV>(acc, r);
+        pin(cur);
+        consume_point<DT, NV>(acc, cur);
         fence_sched();
+        cur = nxt;
     }
 }
 
