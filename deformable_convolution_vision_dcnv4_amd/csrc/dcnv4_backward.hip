@@ -23,6 +23,8 @@
 // them.  x's gradient is a scatter: hardware fp32 atomic adds into a buffer
 // this library zeroes first (its summation order is not fixed).
 
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 
@@ -385,6 +387,233 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
     }
 }
 
+// First output index along one axis whose clamped grid centre
+// min(max(o * stride + c0, 0), in - 1) is at least lim (`outs` if none).
+__device__ __forceinline__ int first_output(int lim, int c0, int stride, int in, int outs)
+{
+    if (lim <= 0) return 0;
+    if (lim > in - 1) return outs;
+    const int d = lim - c0;
+    const int o = d >= 0 ? (d + stride - 1) / stride : -((-d) / stride);
+    return min(max(o, 0), outs);
+}
+
+// x's gradient of one (image, group, chunk of CC channels, tile of TS x TS
+// pixels), for images whose bordered plane does not fit in LDS.  A unit's
+// centre is the middle point of its sampling grid, clamped into the image;
+// its home tile holds the centre.  The workgroup visits the units whose
+// centre lies within `margin` pixels of its tile and accumulates, in an LDS
+// copy of the tile (64-bit fixed point as above, F per workgroup from the
+// units it visits), the terms of their corners inside the tile.  A corner in
+// another tile is that tile's when its workgroup visits the unit too; if not,
+// the unit's home workgroup adds the term to grad_x with a global binary32
+// atomic add.  Each term is added once.  grad_x is zeroed beforehand and every
+// tile adds its sums with atomic adds as well (global terms from other tiles
+// may land on the same elements): an element without global terms is exactly
+// its fixed-point sum, rounded once; the others are summed in no fixed order.
+template <int DT, int RC, int CC>
+__global__ void __launch_bounds__(1024) k_backward_x_tiled(BArgs a, uint32_t total_blocks, uint32_t per_xcd)
+{
+    using E = Elem<DT>;
+    constexpr int s = E::kBytes;
+    constexpr int P = 9 - RC;                 // K = 3
+    extern __shared__ unsigned long long acc[];
+    __shared__ float red[2][16];
+    __shared__ bool flag[16];
+    const int chunks = a.Cg / CC;
+    uint32_t b;
+    if (!logical_block(blockIdx.x, total_blocks, per_xcd, &b)) return;
+    // b = ((n * tiles + t) * G + g) * chunks + ch: the groups and chunks of a
+    // tile, which read the same offset and weight rows, on one XCD
+    const uint32_t gc = (uint32_t)(a.G * chunks);
+    const uint32_t nt = b / gc, r = b - nt * gc;
+    const uint32_t ntiles = (uint32_t)(a.tiles_y * a.tiles_x);
+    const uint32_t n = nt / ntiles, t = nt - n * ntiles;
+    const uint32_t g = r / (uint32_t)chunks, ch = r - g * (uint32_t)chunks;
+    const int sh = a.tile_sh, TS = 1 << sh, TP = TS * TS;
+    const int tyi = (int)t / a.tiles_x, txi = (int)t - tyi * a.tiles_x;
+    const int ty0 = tyi << sh, tx0 = txi << sh;
+    const int th = min(TS, a.H - ty0), tw = min(TS, a.W - tx0);
+    for (int i = threadIdx.x; i < TP * CC; i += blockDim.x) acc[i] = 0ull;
+
+    // the visited units: output rectangle [hlo, hhi) x [wlo, whi)
+    const int M = a.margin;
+    const int c0 = a.dil - a.pad;             // grid centre of output 0
+    const int hlo = first_output(ty0 - M, c0, a.stride, a.H, a.Ho);
+    const int hhi = max(hlo, first_output(ty0 + TS + M, c0, a.stride, a.H, a.Ho));
+    const int wlo = first_output(tx0 - M, c0, a.stride, a.W, a.Wo);
+    const int whi = max(wlo, first_output(tx0 + TS + M, c0, a.stride, a.W, a.Wo));
+    const int wcnt = whi - wlo;
+    const int nunits = (hhi - hlo) * wcnt;
+
+    const char* oimg = static_cast<const char*>(a.off) + (int64_t)n * a.img_off_elems * s;
+    const char* mimg = static_cast<const char*>(a.msk) + (int64_t)n * a.img_mask_elems * s;
+    const char* gimg = static_cast<const char*>(a.gout) + (int64_t)n * a.img_out_elems * s;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(oimg, a.img_off_bytes);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mimg, a.img_mask_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gimg, a.img_out_bytes);
+    const int64_t chan0 = (int64_t)g * a.Cg + (int64_t)ch * CC;
+
+    // ---- the scale: max|m| and max|g| over the visited units and the chunk
+    float mm = 0.0f, mg = 0.0f;
+    bool bad = false;
+    for (int i = threadIdx.x; i < nunits; i += blockDim.x) {
+        const int hh = i / wcnt;
+        const int pix = (hlo + hh) * a.Wo + wlo + (i - hh * wcnt);
+        RowLoad<DT, P> mrow;
+        RowLoad<DT, CC> grow;
+        mrow.load(rm, (uint32_t)(((int64_t)pix * a.mask_row + (int64_t)g * P) * s));
+        grow.load(rg, (uint32_t)(((int64_t)pix * a.C + chan0) * s));
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const float v = mrow.get(k);
+            mm = fmaxf(mm, fabsf(v));
+            bad |= !isfinite(v);
+        }
+#pragma unroll
+        for (int c = 0; c < CC; ++c) {
+            const float v = grow.get(c);
+            mg = fmaxf(mg, fabsf(v));
+            bad |= !isfinite(v);
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        mm = fmaxf(mm, __shfl_xor(mm, off));
+        mg = fmaxf(mg, __shfl_xor(mg, off));
+    }
+    const bool wave_bad = __any(bad);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { red[0][wave] = mm; red[1][wave] = mg; flag[wave] = wave_bad; }
+    __syncthreads();
+    mm = 0.0f; mg = 0.0f;
+    bool fixed = true;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        mm = fmaxf(mm, red[0][w]);
+        mg = fmaxf(mg, red[1][w]);
+        fixed = fixed & !flag[w];
+    }
+    const float Mv = mm * mg;
+    fixed = fixed & isfinite(Mv);
+    int F = 0;
+    if (fixed && Mv > 0.0f) {
+        // terms per element: at most (visited units) * P points * 4 corners
+        const int64_t terms = (int64_t)nunits * P * 4;
+        int cbits = 0;
+        while (((int64_t)1 << cbits) < terms) ++cbits;
+        int e;
+        frexpf(Mv, &e);                       // Mv < 2^e
+        F = (cbits < 11 ? 51 : 62 - cbits) - e;
+    }
+
+    const double scaleF = ldexp(1.0, F);
+    const float fW = (float)a.W, fH = (float)a.H;
+    float* accf = reinterpret_cast<float*>(acc);
+    float* gxi = a.gx + (int64_t)n * a.img_x_elems + chan0;
+    for (int i = threadIdx.x; i < nunits; i += blockDim.x) {
+        const int hh = i / wcnt;
+        const int ho = hlo + hh, wo = wlo + (i - hh * wcnt);
+        const int pix = ho * a.Wo + wo;
+        RowLoad<DT, 2 * P> orow;
+        RowLoad<DT, P> mrow;
+        RowLoad<DT, CC> grow;
+        orow.load(ro, (uint32_t)(((int64_t)pix * a.off_row + (int64_t)g * 2 * P) * s));
+        mrow.load(rm, (uint32_t)(((int64_t)pix * a.mask_row + (int64_t)g * P) * s));
+        grow.load(rg, (uint32_t)(((int64_t)pix * a.C + chan0) * s));
+        float gr[CC];
+        double gd[CC];
+#pragma unroll
+        for (int c = 0; c < CC; ++c) {
+            gr[c] = grow.get(c);
+            gd[c] = (double)gr[c];
+        }
+        const int cy = min(max(ho * a.stride + c0, 0), a.H - 1);
+        const int cx = min(max(wo * a.stride + c0, 0), a.W - 1);
+        const bool home = (cy >> sh) == tyi && (cx >> sh) == txi;
+        const int bx0 = wo * a.stride - a.pad, by0 = ho * a.stride - a.pad;
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int q = (RC && k >= 4) ? k + 1 : k;
+            const int i3 = q / 3, j3 = q % 3;
+            const float px = fmaf(orow.get(k), a.offset_scale, (float)(bx0 + j3 * a.dil));
+            const float py = fmaf(orow.get(P + k), a.offset_scale, (float)(by0 + i3 * a.dil));
+            const float m = mrow.get(k);
+            if (!((px > -1.0f) & (px < fW) & (py > -1.0f) & (py < fH))) continue;
+            const float fx = floorf(px), fy = floorf(py);
+            const int x0 = (int)fx, y0 = (int)fy;
+            const float lx = px - fx, ly = py - fy;
+            const float hx = 1.0f - lx, hy = 1.0f - ly;
+            const float mhy = m * hy, mly = m * ly;
+            const float w[4] = {mhy * hx, mhy * lx, mly * hx, mly * lx};
+            const int ry = y0 - ty0, rx = x0 - tx0;
+            const bool iny[2] = {(unsigned)ry < (unsigned)th, (unsigned)(ry + 1) < (unsigned)th};
+            const bool inx[2] = {(unsigned)rx < (unsigned)tw, (unsigned)(rx + 1) < (unsigned)tw};
+#pragma unroll
+            for (int cr = 0; cr < 4; ++cr) {
+                const int dy = cr >> 1, dx = cr & 1;
+                if (iny[dy] & inx[dx]) {
+                    const int cell = (ry + dy) * TS + rx + dx;
+                    if (fixed) {
+                        // the exact term rounded to the grid of 2^-F, as in k_backward_x
+                        constexpr double kMagic = 0x1.8p52;
+                        constexpr unsigned long long kMagicBits = 0x4338000000000000ull;
+                        const double wd = (double)w[cr] * scaleF;
+#pragma unroll
+                        for (int c = 0; c < CC; ++c) {
+                            const double tv = wd * gd[c] + kMagic;
+                            atomicAdd(&acc[c * TP + cell], (unsigned long long)__double_as_longlong(tv) - kMagicBits);
+                        }
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < CC; ++c) atomicAdd(&accf[c * TP + cell], w[cr] * gr[c]);
+                    }
+                } else if (home) {
+                    const int qy = y0 + dy, qx = x0 + dx;
+                    // the corner's tile visits this unit iff the centre is within its margin
+                    const bool reached = (unsigned)(cy - ((qy >> sh) << sh) + M) < (unsigned)(TS + 2 * M) &&
+                                         (unsigned)(cx - ((qx >> sh) << sh) + M) < (unsigned)(TS + 2 * M);
+                    if ((unsigned)qy < (unsigned)a.H && (unsigned)qx < (unsigned)a.W && !reached) {
+                        float* dst = gxi + ((int64_t)qy * a.W + qx) * a.C;
+#pragma unroll
+                        for (int c = 0; c < CC; ++c) unsafeAtomicAdd(dst + c, w[cr] * gr[c]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // the tile's sums into grad_x[n, y, x, g*Cg + ch*CC + c]
+    const int cells = th * tw * CC;
+    for (int i = threadIdx.x; i < cells; i += blockDim.x) {
+        const int c = i % CC, p = i / CC;
+        const int yy = p / tw, xx = p - (p / tw) * tw;
+        const int idx = c * TP + yy * TS + xx;
+        const float v = fixed ? (float)ldexp((double)(long long)acc[idx], -F) : accf[idx];
+        unsafeAtomicAdd(gxi + ((int64_t)(ty0 + yy) * a.W + tx0 + xx) * a.C + c, v);
+    }
+}
+
+template <int DT, int RC>
+void launch_bxt_cc(const BArgs& a, unsigned total, size_t lds, hipStream_t stream)
+{
+    const uint32_t per_xcd = (total + 7) / 8;
+    const unsigned grid = per_xcd * 8;
+    switch (a.cc) {
+        case 16: hipLaunchKernelGGL((k_backward_x_tiled<DT, RC, 16>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        case 8: hipLaunchKernelGGL((k_backward_x_tiled<DT, RC, 8>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        case 4: hipLaunchKernelGGL((k_backward_x_tiled<DT, RC, 4>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        case 2: hipLaunchKernelGGL((k_backward_x_tiled<DT, RC, 2>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+        default: hipLaunchKernelGGL((k_backward_x_tiled<DT, RC, 1>), dim3(grid), dim3(1024), lds, stream, a, total, per_xcd); break;
+    }
+}
+
+template <int DT>
+void launch_bxt(const BArgs& a, unsigned grid, size_t lds, hipStream_t stream)
+{
+    if (a.remove_center) launch_bxt_cc<DT, 1>(a, grid, lds, stream);
+    else launch_bxt_cc<DT, 0>(a, grid, lds, stream);
+}
+
 template <int DT, int RC>
 void launch_bx_cc(const BArgs& a, unsigned total, size_t lds, hipStream_t stream)
 {
@@ -482,9 +711,16 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     a.div_G = make_fastdiv((uint32_t)p.G);
     a.div_Wo = make_fastdiv((uint32_t)p.Wo);
 
-    // x's gradient in LDS when a channel chunk of the bordered image fits
+    // x's gradient in LDS when a channel chunk of the bordered image fits,
+    // else in LDS tiles (K = 3), else with global atomics only
     a.cc = gx ? backward_x_chunk(p) : 0;
-    if (gx && !a.cc) {
+    const bool whole = a.cc > 0;
+    const bool tiled = gx && !whole && backward_x_tiles(p, &a.cc, &a.tile_sh, &a.margin);
+    if (tiled) {
+        a.tiles_y = (p.H + (1 << a.tile_sh) - 1) >> a.tile_sh;
+        a.tiles_x = (p.W + (1 << a.tile_sh) - 1) >> a.tile_sh;
+    }
+    if (gx && !whole) {
         const int64_t n = (int64_t)p.N * a.img_x_elems;
         const int64_t blocks = ceil_div(ceil_div(n, 4), 256);
         hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, gx, n);
@@ -495,7 +731,7 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     // when it fits, unless x's gradient needs the atomics kernel anyway
     int wblock = 0, wpitch = 0;
     size_t wlds = 0;
-    const bool om_window = (goff || gmask) && (a.cc || !gx) && backward_om_window_plan(p, gout, &wblock, &wpitch, &wlds);
+    const bool om_window = (goff || gmask) && (whole || !gx) && backward_om_window_plan(p, gout, &wblock, &wpitch, &wlds);
     if (om_window) {
         BArgs b = a;
         b.gx = nullptr;
@@ -503,9 +739,9 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
         const hipError_t e = launch_backward_om_window(b, p.dtype, p.Cg * s / 16, wblock, wlds, stream);
         if (e != hipSuccess) return e;
     }
-    if ((!om_window && (goff || gmask)) || (gx && !a.cc)) {
+    if ((!om_window && (goff || gmask)) || (gx && !whole && !tiled)) {
         BArgs b = a;
-        if (a.cc) b.gx = nullptr;          // the LDS kernel below takes x's gradient
+        if (whole || tiled) b.gx = nullptr;   // an LDS kernel below takes x's gradient
         if (om_window) b.goff = b.gmask = nullptr;
         const int64_t grid = ceil_div(a.units_total, 4 * (int64_t)a.units_per_wave);
         hipError_t e = hipErrorInvalidValue;
@@ -517,7 +753,18 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
         }
         if (e != hipSuccess) return e;
     }
-    if (a.cc) {
+    if (tiled) {
+        const unsigned grid = (unsigned)((int64_t)p.N * a.tiles_y * a.tiles_x * p.G * (p.Cg / a.cc));
+        const size_t lds = ((size_t)1 << (2 * a.tile_sh)) * a.cc * 8;
+        switch (p.dtype) {
+            case DCNV4_F32: launch_bxt<DCNV4_F32>(a, grid, lds, stream); break;
+            case DCNV4_F16: launch_bxt<DCNV4_F16>(a, grid, lds, stream); break;
+            case DCNV4_BF16: launch_bxt<DCNV4_BF16>(a, grid, lds, stream); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    if (whole) {
         // terms per x element: at most (units of the image) * P points * 4 corners
         const int64_t terms = (int64_t)p.Ho * p.Wo * p.P * 4;
         int cb = 0;
@@ -534,6 +781,36 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin)
+{
+    // K = 3: tiles of 64 x 64 pixels, the most channels per workgroup (a
+    // power of two dividing Cg, at most 16) whose tile of 64-bit accumulators
+    // fits in LDS, and the units of a 16-pixel margin around the tile.  The
+    // margin trades visits against global atomic adds: with offsets of 8
+    // pixels' spread (256 x 256 images) 16 pixels measured fastest, ahead of
+    // 12 (atomic adds) and 20 or more (visits)
+    if (p.K != 3) return false;
+    int sh = 6, m = 16;
+    // DCNV4_BWD_TILE="<log2 side>,<margin>" overrides both (side 8 to 128, margin 0 to 256)
+    if (const char* env = getenv("DCNV4_BWD_TILE")) {
+        int es = 0, em = 0;
+        if (sscanf(env, "%d,%d", &es, &em) == 2 && es >= 3 && es <= 7 && em >= 0 && em <= 256) {
+            sh = es;
+            m = em;
+        }
+    }
+    const int64_t cell = ((int64_t)1 << (2 * sh)) * 8;
+    for (int c = 16; c >= 1; c /= 2) {
+        if (p.Cg % c == 0 && cell * c <= kLdsPerCu) {
+            *cc = c;
+            *tile_sh = sh;
+            *margin = m;
+            return true;
+        }
+    }
+    return false;
 }
 
 int backward_x_chunk(const Problem& p)

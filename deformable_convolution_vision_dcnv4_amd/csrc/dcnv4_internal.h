@@ -57,6 +57,9 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
 int backward_vec_bytes(const Problem& p, const void* gout);
 // Channels per workgroup of the LDS x-gradient kernel (0: global atomics instead).
 int backward_x_chunk(const Problem& p);
+// When the whole image does not fit: the tiled LDS x-gradient kernel's
+// channels per workgroup, log2 tile side and margin (false: global atomics).
+bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin);
 // Whether the offset/weight gradients can read their corners from an LDS copy
 // of each (image, group) (K = 3, one or two 16-byte vectors per unit, 16-byte
 // aligned x and output gradient, the bordered image within the LDS), and

@@ -96,6 +96,9 @@ struct BArgs {
     int cc;                         // x-gradient LDS kernel: channels per workgroup (0 = atomics path)
     int cbits;                      // x-gradient LDS kernel: log2 bound of the terms per element
     int pitch;                      // offset/weight-gradient LDS kernel: window row pitch (16-byte entries)
+    int tile_sh;                    // tiled x-gradient kernel: log2 of the square tile's side (0 = whole image)
+    int tiles_y, tiles_x;           // tiled x-gradient kernel: tiles per image along each axis
+    int margin;                     // tiled x-gradient kernel: pixels around a tile whose units it visits
     uint32_t units_img;
     int64_t units_total;
     FastDiv div_units_img, div_G, div_Wo;

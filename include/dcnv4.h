@@ -151,8 +151,13 @@ int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, v
  * to a multiple of 2^-F and summed exactly in
  * 64-bit integers (reproducible; F per (image, group) from the largest
  * |weight| * |grad_out| and the term count, so sums cannot overflow; the
- * binary32 path if either holds a non-finite value); otherwise summed with
- * hardware atomic adds, whose order is not fixed.  Gradients must not
+ * binary32 path if either holds a non-finite value).  For K = 3 and larger
+ * images the same is done per 64 x 64-pixel tile (F per tile), for the units
+ * whose grid centre lies within 16 pixels of the tile; terms from units
+ * farther away are added with hardware atomic adds, so elements that receive
+ * such terms are summed in no fixed order (environment DCNV4_BWD_TILE=
+ * "<log2 side>,<margin>" changes both: side 8..128, margin 0..256).  Other
+ * kernel sizes: hardware atomic adds, whose order is not fixed.  Gradients must not
  * overlap the inputs or grad_x; grad_offset and grad_mask may interleave
  * (one packed tensor) but must not share elements.  Needs Cg*s <= 64 vectors
  * of the widest width the pointers allow (else DCNV4_ERR_TOO_LARGE).

@@ -130,6 +130,34 @@ def test_backward_workloads(name, dtype):
     check(WORKLOADS[name], dtype)
 
 
+# Images whose bordered plane of 64-bit accumulators exceeds the LDS even for
+# one channel ((H + 2) * (W + 2) * 8 > 160 KiB): x's gradient in 64 x 64 LDS
+# tiles with ragged last tiles, corners beyond a tile's margin by global atomic
+# adds.  The last case shrinks the tiles to 8 x 8 with a 2-pixel margin (the
+# library's DCNV4_BWD_TILE setting), so that most terms take the global path.
+TILED = [
+    (Workload("bwd_tiled", 1, 150, 147, 2, 8, ("f32",), offset_dist=("normal", 8.0),
+              mask_dist=("uniform", -1.0, 1.0), seed=54), "f32", None),
+    (Workload("bwd_tiled", 2, 131, 160, 2, 16, ("bf16",), offset_dist=("normal", 8.0),
+              mask_dist=("uniform", -1.0, 1.0), seed=55), "bf16", None),
+    (Workload("bwd_tiled_rc", 1, 150, 150, 1, 4, ("f16",), offset_dist=("normal", 4.0), remove_center=True,
+              seed=56), "f16", None),
+    (Workload("bwd_tiled_geom", 1, 160, 150, 2, 2, ("f32",), offset_dist=("normal", 6.0), stride=2, pad=2, dil=2,
+              offset_scale=0.75, seed=57), "f32", None),
+    (Workload("bwd_tiled_small", 1, 150, 147, 1, 4, ("f32",), offset_dist=("normal", 8.0), seed=58), "f32", "3,2"),
+]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: f"{c[1]}-{c[0].H}x{c[0].W}-G{c[0].G}-Cg{c[0].Cg}-s{c[0].stride}"
+                                                       f"{'-rc' if c[0].remove_center else ''}"
+                                                       f"{'-tile' + c[2].replace(',', '_') if c[2] else ''}")
+def test_backward_tiled_x_gradient(case, monkeypatch):
+    wl, dtype, tile = case
+    if tile:
+        monkeypatch.setenv("DCNV4_BWD_TILE", tile)
+    check(wl, dtype)
+
+
 def test_backward_offset_and_mask_gradients_are_reproducible():
     wl = Workload("bwd_rep", 2, 16, 16, 4, 16, ("f16",), offset_dist=("normal", 2.0), seed=46)
     x, off, m = gen.make_inputs(wl, "f16")
@@ -142,10 +170,12 @@ def test_backward_offset_and_mask_gradients_are_reproducible():
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
 
 
-def test_backward_non_finite_weight_propagates():
-    """A NaN weight: that (image, group) takes the binary32 path and the NaN
-    reaches exactly the pixels the oracle's gradient has NaN at."""
-    wl = Workload("bwd_nan", 2, 10, 11, 2, 8, ("f32",), offset_dist=("normal", 1.5), seed=50)
+@pytest.mark.parametrize("H,W", [(10, 11), (150, 147)], ids=["whole", "tiled"])
+def test_backward_non_finite_weight_propagates(H, W):
+    """A NaN weight: that (image, group) (or the tiles that visit the unit)
+    takes the binary32 path and the NaN reaches exactly the pixels the
+    oracle's gradient has NaN at."""
+    wl = Workload("bwd_nan", 2, H, W, 2, 8, ("f32",), offset_dist=("normal", 1.5), seed=50)
     x, off, m = gen.make_inputs(wl, "f32")
     go = grad_out_for(wl, "f32", 51)
     m = m.copy()
