@@ -729,14 +729,16 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     }
     // offset and weight gradients from an LDS copy of each (image, group)
     // when it fits, unless x's gradient needs the atomics kernel anyway
-    int wblock = 0, wpitch = 0;
-    size_t wlds = 0;
-    const bool om_window = (goff || gmask) && (whole || !gx) && backward_om_window_plan(p, gout, &wblock, &wpitch, &wlds);
+    OmPlan om;
+    const bool om_window = (goff || gmask) && (whole || tiled || !gx) && backward_om_window_plan(p, gout, &om);
     if (om_window) {
         BArgs b = a;
         b.gx = nullptr;
-        b.pitch = wpitch;
-        const hipError_t e = launch_backward_om_window(b, p.dtype, p.Cg * s / 16, wblock, wlds, stream);
+        b.pitch = om.pitch;
+        b.om_th = om.th; b.om_tw = om.tw; b.om_ry = om.ry; b.om_rx = om.rx;
+        b.om_wh = om.wh; b.om_ww = om.ww; b.om_tiles_y = om.tiles_y; b.om_tiles_x = om.tiles_x;
+        b.div_om_tw = make_fastdiv((uint32_t)om.tw);
+        const hipError_t e = launch_backward_om_window(b, p.dtype, p.Cg * s / 16, om.block, om.lds, stream);
         if (e != hipSuccess) return e;
     }
     if ((!om_window && (goff || gmask)) || (gx && !whole && !tiled)) {

@@ -22,6 +22,9 @@
 // per XCD so that an image's groups, whose rows share cache lines, meet in
 // one L2.  The results are deterministic (a fixed operation order).
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
 #include "dcnv4_kernels.h"
@@ -73,8 +76,20 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
 
     uint32_t lb;
     if (!logical_block(blockIdx.x, total_blocks, per_xcd, &lb)) return;
-    const uint32_t n = fdiv(lb, a.div_G);
-    const uint32_t g = lb - n * (uint32_t)a.G;
+    // logical block = (n * tiles + t) * G + g: the groups of a tile, whose
+    // pixels share cache lines, side by side
+    const uint32_t nt = fdiv(lb, a.div_G);
+    const uint32_t g = lb - nt * (uint32_t)a.G;
+    const uint32_t ntiles = (uint32_t)(a.om_tiles_y * a.om_tiles_x);
+    const uint32_t n = nt / ntiles, t = nt - n * ntiles;
+    const int ty = (int)t / a.om_tiles_x, tx = (int)t - ty * a.om_tiles_x;
+    const int oy0 = ty * a.om_th, ox0 = tx * a.om_tw;
+    const int th = min(a.om_th, a.Ho - oy0), tw = min(a.om_tw, a.Wo - ox0);
+    // the window: pixels [wy0, wy0 + wh) x [wx0, wx0 + ww) of the zero-bordered image
+    const int wy0 = max(-1, oy0 * a.stride - a.pad - a.om_ry);
+    const int wx0 = max(-1, ox0 * a.stride - a.pad - a.om_rx);
+    const int wh = max(0, min(a.om_wh, a.H + 1 - wy0));
+    const int ww = max(0, min(a.om_ww, a.W + 1 - wx0));
 
     const char* xs = static_cast<const char*>(a.x) + (int64_t)n * a.img_x_elems * s;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs, a.img_x_bytes);
@@ -88,14 +103,14 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
     const uint32_t row_bytes = (uint32_t)a.W * pix_bytes;
     const uint32_t grp_bytes = g * (uint32_t)a.Cg * s;
 
-    // ---- the window: entry (plane v, row r, column c) holds image pixel
-    // (r - 1, c - 1), channels [v * EPV, v * EPV + EPV) of group g; zero off
-    // the image.  Chunk q = pixel entry q / NV, plane q % NV: consecutive
-    // lanes read consecutive 16-byte pieces of x.
+    // ---- staging: entry (plane v, row r, column c) holds pixel (wy0 + r,
+    // wx0 + c), channels [v * EPV, v * EPV + EPV) of group g; zero off the
+    // image.  Chunk q = pixel q / NV, plane q % NV: consecutive lanes read
+    // consecutive 16-byte pieces of x.
     const uint32_t pitch = (uint32_t)a.pitch;
-    const uint32_t WH = (uint32_t)a.H + 2;
-    const uint32_t plane16 = WH * pitch;
-    const uint32_t nchunks = plane16 * NV;
+    const uint32_t plane16 = (uint32_t)a.om_wh * pitch;
+    const uint32_t uww = (uint32_t)ww;
+    const uint32_t nchunks = (uint32_t)wh * uww * NV;
     {
         constexpr int U = 8;
         for (uint32_t c0 = threadIdx.x; c0 < nchunks; c0 += B * U) {
@@ -106,12 +121,12 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
                 const uint32_t c = c0 + r * B;
                 const uint32_t p = c / NV;
                 const uint32_t cv = c - p * NV;
-                const uint32_t wy = p / pitch, wx = p - wy * pitch;
-                const int y = (int)wy - 1, x = (int)wx - 1;
+                const uint32_t wy = p / uww, wx = p - wy * uww;
+                const int y = wy0 + (int)wy, x = wx0 + (int)wx;
                 const bool in = (c < nchunks) & (y >= 0) & (y < a.H) & (x >= 0) & (x < a.W);
                 const uint32_t voff = (uint32_t)y * row_bytes + (uint32_t)x * pix_bytes + grp_bytes + cv * 16u;
                 v[r] = buf_load16(rx, in ? voff : kOobOffset);
-                dst[r] = cv * plane16 + p;
+                dst[r] = cv * plane16 + wy * pitch + wx;
             }
 #pragma unroll
             for (int r = 0; r < U; ++r)
@@ -124,9 +139,10 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
     const int row16 = (int)pitch * 16;
     const int plane = (int)plane16 * 16;
     const float fW = (float)a.W, fH = (float)a.H;
-    // a point that contributes nothing reads the zero columns W + 1, W + 2
-    const float zx = (float)(a.W + 1), zy = -1.0f;
-    const uint32_t units = (uint32_t)(a.Ho * a.Wo);
+    // a point whose four corners lie in the window: wx0 <= px < wx0 + ww - 1 (same for y)
+    const float wxl = (float)wx0, wxh = (float)(wx0 + ww - 1);
+    const float wyl = (float)wy0, wyh = (float)(wy0 + wh - 1);
+    const uint32_t units = (uint32_t)(th * tw);
     const float scale = a.offset_scale;
 
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
@@ -136,10 +152,13 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
     const int pi = q / 3, pj = q % 3;
     const uint32_t upass = (B >> 6) * UPW;     // units per pass of the workgroup
     for (uint32_t u0 = wave * UPW; u0 < units; u0 += upass) {
-        const uint32_t u = u0 + ul;
-        if (ul >= UPW || u >= units) continue;
-        const uint32_t oy = fdiv(u, a.div_Wo);
-        const uint32_t ox = u - oy * (uint32_t)a.Wo;
+        const uint32_t ut = u0 + ul;
+        if (ul >= UPW || ut >= units) continue;
+        // row within the tile (the last tile of a row may be narrower)
+        const uint32_t ry = tw == a.om_tw ? fdiv(ut, a.div_om_tw) : ut / (uint32_t)tw;
+        const uint32_t oy = (uint32_t)oy0 + ry;
+        const uint32_t ox = (uint32_t)ox0 + (ut - ry * (uint32_t)tw);
+        const uint32_t u = oy * (uint32_t)a.Wo + ox;
         const int64_t prow = (int64_t)u * a.off_row + (int64_t)g * 2 * P;     // within the image
         const int64_t mrow = (int64_t)u * a.mask_row + (int64_t)g * P;
         float dx, dy, m;
@@ -157,24 +176,46 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
 #pragma unroll
         for (int v = 0; v < NV; ++v) gv[v] = buf_load16(rg, go + 16u * v);
 
-        float px = fmaf(dx, scale, (float)((int)ox * a.stride - a.pad + pj * a.dil));
-        float py = fmaf(dy, scale, (float)((int)oy * a.stride - a.pad + pi * a.dil));
+        const float px = fmaf(dx, scale, (float)((int)ox * a.stride - a.pad + pj * a.dil));
+        const float py = fmaf(dy, scale, (float)((int)oy * a.stride - a.pad + pi * a.dil));
         const bool valid = (px > -1.0f) & (px < fW) & (py > -1.0f) & (py < fH);
-        px = valid ? px : zx;
-        py = valid ? py : zy;
-        const float fx = floorf(px), fy = floorf(py);
-        const float lx = px - fx, ly = py - fy;
+        const bool inwin = (px >= wxl) & (px < wxh) & (py >= wyl) & (py < wyh);
+        const float pxs = valid ? px : wxl, pys = valid ? py : wyl;
+        const float fx = floorf(pxs), fy = floorf(pys);
+        const float lx = pxs - fx, ly = pys - fy;
         const float hx = 1.0f - lx, hy = 1.0f - ly;
-        // window entry of corner (y0, x0): (y0 + 1, x0 + 1)
-        const int a00 = ((int)fy + 1) * row16 + (((int)fx + 1) << 4);
-        float A00 = 0.0f, A01 = 0.0f, A10 = 0.0f, A11 = 0.0f;
+        const int x0 = (int)fx, y0 = (int)fy;
+        // window entry of corner (y0, x0); a point outside the window reads
+        // entry 0 (a valid one then reads its corners from global memory,
+        // a skipped one's gradients are zero whatever it reads)
+        const int a00 = (valid & inwin) ? (y0 - wy0) * row16 + ((x0 - wx0) << 4) : 0;
+        u32x4 cv[NV][4];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const char* p0 = lbase + a00 + v * plane;
-            const u32x4 c00 = *reinterpret_cast<const u32x4*>(p0);
-            const u32x4 c01 = *reinterpret_cast<const u32x4*>(p0 + 16);
-            const u32x4 c10 = *reinterpret_cast<const u32x4*>(p0 + row16);
-            const u32x4 c11 = *reinterpret_cast<const u32x4*>(p0 + row16 + 16);
+            cv[v][0] = *reinterpret_cast<const u32x4*>(p0);
+            cv[v][1] = *reinterpret_cast<const u32x4*>(p0 + 16);
+            cv[v][2] = *reinterpret_cast<const u32x4*>(p0 + row16);
+            cv[v][3] = *reinterpret_cast<const u32x4*>(p0 + row16 + 16);
+        }
+        if (valid & !inwin) {
+            // corners from global memory, zero off the image
+            const bool iny0 = y0 >= 0, iny1 = y0 + 1 < a.H, inx0 = x0 >= 0, inx1 = x0 + 1 < a.W;
+            const uint32_t base = (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + grp_bytes;
+            const uint32_t off[4] = {(iny0 & inx0) ? base : kOobOffset,
+                                     (iny0 & inx1) ? base + pix_bytes : kOobOffset,
+                                     (iny1 & inx0) ? base + row_bytes : kOobOffset,
+                                     (iny1 & inx1) ? base + row_bytes + pix_bytes : kOobOffset};
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+#pragma unroll
+                for (int cr = 0; cr < 4; ++cr)
+                    cv[v][cr] = buf_load16(rx, off[cr] == kOobOffset ? kOobOffset : off[cr] + 16u * v);
+            }
+        }
+        float A00 = 0.0f, A01 = 0.0f, A10 = 0.0f, A11 = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
             float gr[EPV];
             const uint32_t w[4] = {gv[v].x, gv[v].y, gv[v].z, gv[v].w};
 #pragma unroll
@@ -182,10 +223,10 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
                 if constexpr (s == 4) gr[e] = __uint_as_float(w[e]);
                 else gr[e] = E::raw_to_f((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
             }
-            A00 = dot_vec16<DT>(A00, gr, c00);
-            A01 = dot_vec16<DT>(A01, gr, c01);
-            A10 = dot_vec16<DT>(A10, gr, c10);
-            A11 = dot_vec16<DT>(A11, gr, c11);
+            A00 = dot_vec16<DT>(A00, gr, cv[v][0]);
+            A01 = dot_vec16<DT>(A01, gr, cv[v][1]);
+            A10 = dot_vec16<DT>(A10, gr, cv[v][2]);
+            A11 = dot_vec16<DT>(A11, gr, cv[v][3]);
         }
         float sm = (hy * hx) * A00;
         sm = fmaf(hy * lx, A01, sm);
@@ -228,31 +269,65 @@ hipError_t launch_nv(const BArgs& a, int nv, int block, uint32_t total, size_t l
 
 }  // namespace
 
-bool backward_om_window_plan(const Problem& p, const void* gout, int* block, int* pitch, size_t* lds)
+bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
 {
     const int s = p.dtype == DCNV4_F32 ? 4 : 2;
     if (p.K != 3 || (p.Cg * s) % 16) return false;
     const int nv = p.Cg * s / 16;
     if (nv > 2) return false;
     if ((uintptr_t)p.x % 16 || (uintptr_t)gout % 16) return false;
-    // at least two zero columns past the image's right border, rows a whole
-    // number of 16-entry bank groups apart (as the forward's windows)
-    const int pt = (p.W + 2 + 2 + 15) / 16 * 16;
-    const int64_t bytes = (int64_t)(p.H + 2) * pt * nv * 16;
-    if (bytes > kLdsPerCu) return false;
-    const int64_t units = (int64_t)p.Ho * p.Wo;
-    int b = (int)((units + 63) / 64 * 64);
-    if (b > 1024) b = 1024;
-    *block = b;
-    *pitch = pt;
-    *lds = (size_t)bytes;
+    // the whole zero-bordered image when it fits, rows a whole number of
+    // 16-entry bank groups apart (as the forward's windows)
+    OmPlan o;
+    o.pitch = (p.W + 2 + 15) / 16 * 16;
+    int64_t bytes = (int64_t)(p.H + 2) * o.pitch * nv * 16;
+    if (bytes <= kLdsPerCu) {
+        o.th = p.Ho;
+        o.tw = p.Wo;
+        o.ry = o.rx = p.pad + 1;              // the window starts at pixel -1
+        o.wh = p.H + 2;
+        o.ww = p.W + 2;
+        const int64_t units = (int64_t)p.Ho * p.Wo;
+        o.block = (int)(units < 1024 ? (units + 63) / 64 * 64 : 1024);
+    } else {
+        // tiles of th x tw units; the window covers their grid and r pixels
+        // around it, points beyond read their corners from global memory.
+        // DCNV4_BWD_OM="<th>,<tw>,<r>" overrides the shape (1..256, 0..64).
+        int th = 32, tw = 32, r = 8;
+        if (const char* env = getenv("DCNV4_BWD_OM")) {
+            int eh = 0, ew = 0, er = -1;
+            if (sscanf(env, "%d,%d,%d", &eh, &ew, &er) == 3 && eh >= 1 && eh <= 256 && ew >= 1 && ew <= 256 &&
+                er >= 0 && er <= 64) {
+                th = eh;
+                tw = ew;
+                r = er;
+            }
+        }
+        o.th = th < p.Ho ? th : p.Ho;
+        o.tw = tw < p.Wo ? tw : p.Wo;
+        o.ry = o.rx = r;
+        const int64_t eh = (int64_t)(o.th - 1) * p.stride + 2 * p.dil + 2 + 2 * r;
+        const int64_t ew = (int64_t)(o.tw - 1) * p.stride + 2 * p.dil + 2 + 2 * r;
+        o.wh = (int)(eh < p.H + 2 ? eh : p.H + 2);
+        o.ww = (int)(ew < p.W + 2 ? ew : p.W + 2);
+        o.pitch = (o.ww + 15) / 16 * 16;
+        bytes = (int64_t)o.wh * o.pitch * nv * 16;
+        if (bytes > kLdsPerCu) return false;
+        o.block = 1024;
+    }
+    o.tiles_y = (p.Ho + o.th - 1) / o.th;
+    o.tiles_x = (p.Wo + o.tw - 1) / o.tw;
+    o.lds = (size_t)bytes;
+    *plan = o;
     return true;
 }
 
 hipError_t launch_backward_om_window(const BArgs& a, int dtype, int nv, int block, size_t lds,
                                      hipStream_t stream)
 {
-    const uint32_t total = (uint32_t)(a.units_total / a.units_img) * (uint32_t)a.G;   // images x groups
+    // images x tiles x groups
+    const uint32_t total = (uint32_t)(a.units_total / a.units_img) * (uint32_t)(a.om_tiles_y * a.om_tiles_x) *
+                           (uint32_t)a.G;
     switch (dtype) {
         case DCNV4_F32: return launch_nv<DCNV4_F32>(a, nv, block, total, lds, stream);
         case DCNV4_F16: return launch_nv<DCNV4_F16>(a, nv, block, total, lds, stream);

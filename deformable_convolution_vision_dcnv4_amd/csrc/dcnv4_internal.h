@@ -60,11 +60,19 @@ int backward_x_chunk(const Problem& p);
 // When the whole image does not fit: the tiled LDS x-gradient kernel's
 // channels per workgroup, log2 tile side and margin (false: global atomics).
 bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin);
-// Whether the offset/weight gradients can read their corners from an LDS copy
-// of each (image, group) (K = 3, one or two 16-byte vectors per unit, 16-byte
-// aligned x and output gradient, the bordered image within the LDS), and
-// that kernel's workgroup size, window row pitch and LDS bytes.
-bool backward_om_window_plan(const Problem& p, const void* gout, int* block, int* pitch, size_t* lds);
+// Launch shape of the offset/weight-gradient LDS kernel: output tiles of
+// th x tw units (the whole image when its bordered copy fits), windows of
+// wh x ww pixels from ry / rx pixels before a tile's grid, rows of `pitch`
+// 16-byte entries.
+struct OmPlan {
+    int block, pitch;
+    int th, tw, ry, rx, wh, ww, tiles_y, tiles_x;
+    size_t lds;
+};
+// Whether the offset/weight gradients can read their corners from an LDS
+// window of each (image, group) (K = 3, one or two 16-byte vectors per unit,
+// 16-byte aligned x and output gradient, a window that fits the LDS), and how.
+bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan);
 hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
                            hipStream_t stream);
 

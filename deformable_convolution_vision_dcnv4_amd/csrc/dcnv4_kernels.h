@@ -99,15 +99,20 @@ struct BArgs {
     int tile_sh;                    // tiled x-gradient kernel: log2 of the square tile's side (0 = whole image)
     int tiles_y, tiles_x;           // tiled x-gradient kernel: tiles per image along each axis
     int margin;                     // tiled x-gradient kernel: pixels around a tile whose units it visits
+    // offset/weight-gradient LDS kernel: output tiles of om_th x om_tw units
+    // (the whole image when it fits), windows of om_wh x om_ww pixels
+    // starting om_ry / om_rx pixels before the tile's grid
+    int om_th, om_tw, om_ry, om_rx, om_wh, om_ww, om_tiles_y, om_tiles_x;
+    FastDiv div_om_tw;
     uint32_t units_img;
     int64_t units_total;
     FastDiv div_units_img, div_G, div_Wo;
 };
 
 hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hipStream_t stream);
-// Offset/weight gradients with the image of each (image, group) in LDS:
-// N * G workgroups of `block` threads, `lds` bytes of window, 16-byte
-// vectors per unit nv (1 or 2).
+// Offset/weight gradients with a window of each (image, tile, group) in LDS
+// (the tile shape in a.om_*): N * tiles * G workgroups of `block` threads,
+// `lds` bytes of window, 16-byte vectors per unit nv (1 or 2).
 hipError_t launch_backward_om_window(const BArgs& a, int dtype, int nv, int block, size_t lds,
                                      hipStream_t stream);
 hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);

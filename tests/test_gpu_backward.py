@@ -158,6 +158,31 @@ def test_backward_tiled_x_gradient(case, monkeypatch):
     check(wl, dtype)
 
 
+# Offset/weight gradients from LDS windows of output tiles (images whose
+# bordered copy exceeds the LDS), points beyond a window read from global
+# memory; the library's DCNV4_BWD_OM="<th>,<tw>,<margin>" shrinks the tiles
+# and margins so that many points take that path, with ragged last tiles.
+OM_TILED = [
+    (Workload("bwd_om", 1, 100, 97, 2, 4, ("f32",), offset_dist=("normal", 4.0), seed=59), "f32", None),
+    (Workload("bwd_om", 2, 75, 80, 2, 16, ("bf16",), offset_dist=("normal", 6.0), remove_center=True,
+              seed=60), "bf16", None),
+    (Workload("bwd_om", 1, 90, 71, 1, 16, ("f16",), offset_dist=("normal", 3.0), seed=61), "f16", "7,13,0"),
+    (Workload("bwd_om_geom", 1, 120, 110, 2, 4, ("f32",), offset_dist=("normal", 3.0), stride=2, pad=2, dil=2,
+              offset_scale=0.5, seed=62), "f32", "5,9,1"),
+    (Workload("bwd_om", 1, 100, 97, 2, 8, ("f16",), offset_dist=("normal", 8.0), seed=63), "f16", "8,8,1"),
+]
+
+
+@pytest.mark.parametrize("case", OM_TILED, ids=lambda c: f"{c[1]}-{c[0].H}x{c[0].W}-Cg{c[0].Cg}-s{c[0].stride}"
+                                                         f"{'-rc' if c[0].remove_center else ''}"
+                                                         f"{'-om' + c[2].replace(',', '_') if c[2] else ''}")
+def test_backward_tiled_offset_and_mask_gradients(case, monkeypatch):
+    wl, dtype, shape = case
+    if shape:
+        monkeypatch.setenv("DCNV4_BWD_OM", shape)
+    check(wl, dtype)
+
+
 def test_backward_offset_and_mask_gradients_are_reproducible():
     wl = Workload("bwd_rep", 2, 16, 16, 4, 16, ("f16",), offset_dist=("normal", 2.0), seed=46)
     x, off, m = gen.make_inputs(wl, "f16")
