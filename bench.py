@@ -20,6 +20,7 @@ bytes per launch measured by rocprofv3 counters on the same kernel source
 (profiles/<workload>_<dtype>_hbm_counters.json), else null.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -84,6 +85,8 @@ def main():
                     help="forward (the headline), the backward (gradients of x, offsets, weights), or "
                          "softmax (the DCNv3-style aggregation, for comparison)")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's last)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="run the workload's shape at this batch size instead of its own")
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotating input copies")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -107,6 +110,10 @@ def main():
             print("[bench]", *a, file=sys.stderr, flush=True)
 
     wl = WORKLOADS[args.workload]
+    if args.batch is not None and args.batch != wl.N:
+        if args.batch < 1:
+            ap.error("--batch must be at least 1")
+        wl = dataclasses.replace(wl, name=f"{wl.name}_n{args.batch}", N=args.batch)
     dtype = args.dtype or wl.dtypes[-1]
     assert dtype in ("f32", "f16", "bf16")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]

@@ -20,18 +20,24 @@
 //       global reads) make it worse;
 //     - else tiles of 16 x 64 outputs with a margin of 12 pixels (units of
 //       two or more vectors, one lane per vector);
+//   a plan with fewer workgroups than CUs (small batches) takes more bands,
+//   of at least 7 rows, to fill the GPU, else the direct family: a
+//   workgroup holds its CU for its whole tile, so an underfilled grid
+//   leaves CUs idle (batch 1 of the stage-1 shape: 31 us on 4 workgroups
+//   against 6 us for the direct kernel);
 //   units of three or more 16-byte vectors take one lane per vector (measured
 //   8-15% faster than whole-unit lanes, which cap a workgroup at 512
 //   threads); threads per workgroup: the kernel's maximum, or fewer when one
 //   pass covers the tile.  The direct family otherwise.
-// DCNV4_TUNE (environment, read once) overrides the choices for tuning runs:
+// DCNV4_TUNE (environment, parsed again whenever its text changes)
+// overrides the choices for tuning runs and tests; an explicit kernel, tile
+// height or width, group count or full=0|1 turns the GPU-filling rule off:
 // "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1,pitch_add=E,coal=0|1,split=0|1".
 
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
-#include <mutex>
 
 #include "dcnv4.h"
 #include "dcnv4_internal.h"
@@ -45,13 +51,18 @@ struct Tune {
     int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1, pitch_add = 0, coal = -1, split = -1;
 };
 
+// Parsed per thread, again whenever the variable's text changes.
 const Tune& tune()
 {
-    static Tune t;
-    static std::once_flag once;
-    std::call_once(once, [] {
-        const char* env = getenv("DCNV4_TUNE");
-        if (!env) return;
+    thread_local Tune t;
+    thread_local char seen[256] = {1, 0};   // never a variable's text: forces the first parse
+    const char* env = getenv("DCNV4_TUNE");
+    if (!env) env = "";
+    if (strncmp(env, seen, sizeof seen) == 0) return t;
+    strncpy(seen, env, sizeof seen - 1);
+    seen[sizeof seen - 1] = '\0';
+    t = Tune();
+    {
         char buf[256];
         strncpy(buf, env, sizeof buf - 1);
         buf[sizeof buf - 1] = '\0';
@@ -71,11 +82,14 @@ const Tune& tune()
             else if (!strcmp(tok, "coal")) t.coal = atoi(v);
             else if (!strcmp(tok, "split")) t.split = atoi(v);
         }
-    });
+    }
     return t;
 }
 
 int elem_bytes(int dtype) { return dtype == DCNV4_F32 ? 4 : 2; }
+
+// Fewest output rows per band when bands are added to fill the GPU.
+constexpr int kMinBandRows = 7;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -181,6 +195,24 @@ bool plan_window(const Problem& p, Plan* pl)
         }
     }
     if (!GB) return false;
+    // fill the GPU: each workgroup holds one CU for the whole of its tile, so
+    // a plan with fewer workgroups than CUs leaves CUs idle.  Full-width plans
+    // take more bands; bands under kMinBandRows rows cost more in margins than
+    // they save, and there the direct kernel is faster (measured at batch 1 to
+    // 32 of the stage-1 shape and 1 to 4 of the latent shape)
+    if (t.kernel == 0 && t.full < 0 && !t.th && !t.tw && !t.gb) {
+        const int64_t per_band = (int64_t)p.N * ceil_div(p.Wo, TW) * (p.G / GB);
+        if (per_band * ceil_div(p.Ho, TH) < cus) {
+            if (TW < p.Wo) return false;
+            const int th = (int)ceil_div(p.Ho, ceil_div(cus, per_band));
+            if (th < kMinBandRows) return false;
+            if (full) {
+                full = 0;
+                R = t.r >= 0 ? t.r : 5;
+            }
+            TH = th;
+        }
+    }
     if (!full) {
         if (TH > p.Ho) TH = p.Ho;
         if (TW > p.Wo) TW = p.Wo;

@@ -105,7 +105,8 @@ def test_packed_rows_accepted_by_validation():
     (0, 3, 0, 3, "direct", 4), (2, 6, 0, 3, "direct", 4), (0, 16, 8, 3, "direct", 8),
     (1, 16, 0, 5, "direct", 16), (1, 128, 0, 3, "direct", 16)])
 def test_plan_kernel_family_and_read_width(dtype, Cg, xoff, K, kernel, vec):
-    st, pl = plan(dtype=dtype, Cg=Cg, x=X + xoff, K=K, p=K // 2)
+    # a batch that fills the GPU (small batches take the direct kernel, below)
+    st, pl = plan(dtype=dtype, Cg=Cg, x=X + xoff, K=K, p=K // 2, N=64, H=56, W=56)
     assert st == OK
     d = pl.as_dict()
     assert d["kernel"] == kernel
@@ -117,6 +118,35 @@ def test_plan_kernel_family_and_read_width(dtype, Cg, xoff, K, kernel, vec):
         # one lane per unit, or (units of three or more 16-byte vectors) one per vector
         assert pl.lanes_per_unit in (1, Cg * s // 16) and pl.lds_bytes <= 160 * 1024
         assert pl.window_h >= pl.tile_h + 2 and pl.window_w >= pl.tile_w + 2
+
+
+@pytest.mark.parametrize("N,dtype,kernel,tile_h,grid", [
+    (1, 1, "direct", 0, 98), (4, 1, "direct", 0, 392), (8, 1, "window", 7, 256),
+    (16, 1, "window", 14, 256), (32, 1, "window", 28, 256), (64, 1, "window", 56, 256),
+    (8, 0, "window", 7, 256), (64, 0, "window", 19, 768)])
+def test_plan_fills_the_gpu_at_small_batches(N, dtype, kernel, tile_h, grid):
+    """Stage-1 shape (56x56, 4 groups of 16): a whole-image window per
+    (image, group) leaves CUs idle below 64 images, so the plan takes more
+    bands (at least 7 rows) for at least 256 workgroups, else the direct
+    kernel."""
+    st, pl = plan(dtype=dtype, Cg=16, N=N, H=56, W=56, G=4)
+    assert st == OK
+    d = pl.as_dict()
+    assert d["kernel"] == kernel and pl.grid == grid
+    if kernel == "window":
+        assert pl.tile_h == tile_h and pl.tile_w == 56
+
+
+def test_plan_tuning_variable_is_read_again_when_it_changes(monkeypatch):
+    monkeypatch.setenv("DCNV4_TUNE", "kernel=window")
+    st, pl = plan(dtype=1, Cg=16, N=1, H=56, W=56, G=4)
+    assert st == OK and pl.as_dict()["kernel"] == "window" and pl.full_window == 1 and pl.grid == 4
+    monkeypatch.setenv("DCNV4_TUNE", "kernel=direct")
+    st, pl = plan(dtype=1, Cg=16, N=64, H=56, W=56, G=4)
+    assert st == OK and pl.as_dict()["kernel"] == "direct"
+    monkeypatch.delenv("DCNV4_TUNE")
+    st, pl = plan(dtype=1, Cg=16, N=64, H=56, W=56, G=4)
+    assert st == OK and pl.as_dict()["kernel"] == "window" and pl.full_window == 1
 
 
 def test_plan_full_window_for_small_images():

@@ -29,6 +29,18 @@ def _gpu():
     yield
 
 
+@pytest.fixture(params=["auto", "window"], autouse=True)
+def family(request, monkeypatch):
+    """Every test twice: with the planner's own choice (small batches take the
+    direct kernel) and with the window family forced wherever it applies
+    (DCNV4_TUNE=kernel=window), so both families meet every case."""
+    if request.param == "window":
+        monkeypatch.setenv("DCNV4_TUNE", "kernel=window")
+    else:
+        monkeypatch.delenv("DCNV4_TUNE", raising=False)
+    return request.param
+
+
 def run_gpu(x, off, m, dtype, wl=None, **kw):
     xs, os_, ms = gu.dev(x, dtype), gu.dev(off, dtype), gu.dev(m, dtype)
     out = binding.forward(xs, os_, ms, **kw)

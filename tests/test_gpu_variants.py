@@ -41,17 +41,21 @@ def gkw(wl):
 
 
 # (name, N, H, W, G, Cg, offset std, dtypes, expected kernel family, full
-# window).  Units of three or more 16-byte vectors (fp32 Cg=16, 16-bit
-# Cg=24/32/40) take one lane per vector; window_gb holds several groups per
-# workgroup.
+# window, DCNV4_TUNE).  Units of three or more 16-byte vectors (fp32 Cg=16,
+# 16-bit Cg=24/32/40) take one lane per vector; window_gb holds several groups
+# per workgroup.  These batches are too small to fill the GPU, where the
+# planner picks the direct kernel: "kernel=window" keeps the window family's
+# own choices (whole image, bands, groups per workgroup) for them.
 PATHS = [
-    ("window_full", 2, 12, 13, 4, 16, 2.0, ("f32", "f16", "bf16"), "window", 1),
-    ("window_gb", 2, 6, 7, 4, 16, 2.0, ("f32", "bf16"), "window", 1),
-    ("window_full40", 2, 20, 22, 2, 40, 2.0, ("f16", "bf16"), "window", 1),
-    ("window_bands24", 2, 60, 60, 1, 24, 6.0, ("f16",), "window", 0),
-    ("window_bands", 2, 60, 60, 1, 16, 8.0, ("f32",), "window", 0),
-    ("window_bands16", 2, 60, 60, 2, 32, 6.0, ("f16", "bf16"), "window", 0),
-    ("direct", 2, 12, 13, 4, 6, 2.0, ("f32", "f16", "bf16"), "direct", 0),
+    ("window_full", 2, 12, 13, 4, 16, 2.0, ("f32", "f16", "bf16"), "window", 1, "kernel=window"),
+    ("window_gb", 2, 6, 7, 4, 16, 2.0, ("f32", "bf16"), "window", 1, "kernel=window"),
+    ("window_full40", 2, 20, 22, 2, 40, 2.0, ("f16", "bf16"), "window", 1, "kernel=window"),
+    ("window_bands24", 2, 60, 60, 1, 24, 6.0, ("f16",), "window", 0, "kernel=window"),
+    ("window_bands", 2, 60, 60, 1, 16, 8.0, ("f32",), "window", 0, "kernel=window"),
+    ("window_bands16", 2, 60, 60, 2, 32, 6.0, ("f16", "bf16"), "window", 0, "kernel=window"),
+    ("window_fill_bands", 16, 28, 24, 4, 16, 2.0, ("f16",), "window", 0, ""),
+    ("direct", 2, 12, 13, 4, 6, 2.0, ("f32", "f16", "bf16"), "direct", 0, ""),
+    ("direct_small_batch", 2, 12, 13, 4, 16, 2.0, ("f32", "f16"), "direct", 0, ""),
 ]
 CASES = [(p, dt, rc) for p in PATHS for dt in p[7] for rc in (False, True)]
 
@@ -67,8 +71,12 @@ def _plan(wl, dtype, x, off, m):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
-def test_paths_and_remove_center_bit_exact(case):
-    (name, N, H, W, G, Cg, std, _, family, full), dtype, rc = case
+def test_paths_and_remove_center_bit_exact(case, monkeypatch):
+    (name, N, H, W, G, Cg, std, _, family, full, tune), dtype, rc = case
+    if tune:
+        monkeypatch.setenv("DCNV4_TUNE", tune)
+    else:
+        monkeypatch.delenv("DCNV4_TUNE", raising=False)
     wl = Workload(name, N, H, W, G, Cg, (dtype,), offset_dist=("normal", std), mask_dist=("normal", 0.7),
                   remove_center=rc, seed=21)
     x, off, m = gen.make_inputs(wl, dtype)
@@ -83,12 +91,17 @@ def test_paths_and_remove_center_bit_exact(case):
     assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
 
 
+@pytest.mark.parametrize("tune", ["", "kernel=window"], ids=["auto", "window"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("rc", [False, True])
 @pytest.mark.parametrize("Cg", [16, 6])
-def test_packed_offset_mask_rows(dtype, rc, Cg):
+def test_packed_offset_mask_rows(dtype, rc, Cg, tune, monkeypatch):
     """offset = packed[..., :2GP], mask = packed[..., 2GP:3GP] with a row
     stride of 3GP (+ 5 spare elements), consumed in place."""
+    if tune:
+        monkeypatch.setenv("DCNV4_TUNE", tune)
+    else:
+        monkeypatch.delenv("DCNV4_TUNE", raising=False)
     wl = Workload("packed", 2, 11, 12, 4, Cg, (dtype,), offset_dist=("normal", 2.0), remove_center=rc, seed=23)
     x, off, m = gen.make_inputs(wl, dtype)
     G, P = wl.G, wl.P
