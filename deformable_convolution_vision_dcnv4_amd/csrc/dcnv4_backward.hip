@@ -714,6 +714,13 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     // x's gradient in LDS when a channel chunk of the bordered image fits,
     // else in LDS tiles (K = 3), else with global atomics only
     a.cc = gx ? backward_x_chunk(p) : 0;
+    // one workgroup per (image, group, chunk) holds a CU for the whole
+    // image: with at most a quarter as many of them as CUs (small batches),
+    // tiles fill the GPU.  Tiles add visits of the units around them, which
+    // measured slower than the whole image with a third of the CUs busy (the
+    // latent shape at batch 1: 103 against 94 us) and faster with a quarter
+    // (stage-1 shape at batch 4: 50 against 62 us)
+    if (a.cc && backward_fill_gpu() && (int64_t)p.N * p.G * (p.Cg / a.cc) * 4 <= kCus) a.cc = 0;
     const bool whole = a.cc > 0;
     const bool tiled = gx && !whole && backward_x_tiles(p, &a.cc, &a.tile_sh, &a.margin);
     if (tiled) {
@@ -794,7 +801,16 @@ bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin)
     // pixels' spread (256 x 256 images) 16 pixels measured fastest, ahead of
     // 12 (atomic adds) and 20 or more (visits)
     if (p.K != 3) return false;
+    // the largest side from 64 down to 8 whose grid fills the GPU (8 if none does)
     int sh = 6, m = 16;
+    if (backward_fill_gpu()) {
+        for (; sh > 3; --sh) {
+            int c = 16;
+            while (c > 1 && (p.Cg % c || ((int64_t)8 << (2 * sh)) * c > kLdsPerCu)) c /= 2;
+            const int64_t tiles = (int64_t)((p.H + (1 << sh) - 1) >> sh) * ((p.W + (1 << sh) - 1) >> sh);
+            if ((int64_t)p.N * tiles * p.G * (p.Cg / c) >= kCus) break;
+        }
+    }
     // DCNV4_BWD_TILE="<log2 side>,<margin>" overrides both (side 8 to 128, margin 0 to 256)
     if (const char* env = getenv("DCNV4_BWD_TILE")) {
         int es = 0, em = 0;
@@ -813,6 +829,13 @@ bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin)
         }
     }
     return false;
+}
+
+bool backward_fill_gpu()
+{
+    // DCNV4_BWD_FILL=0 keeps the whole-image kernels whenever they fit (tests)
+    const char* env = getenv("DCNV4_BWD_FILL");
+    return !(env && env[0] == '0' && env[1] == '\0');
 }
 
 int backward_x_chunk(const Problem& p)

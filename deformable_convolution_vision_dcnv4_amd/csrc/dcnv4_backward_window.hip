@@ -22,6 +22,7 @@
 // per XCD so that an image's groups, whose rows share cache lines, meet in
 // one L2.  The results are deterministic (a fixed operation order).
 
+#include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -281,7 +282,10 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
     OmPlan o;
     o.pitch = (p.W + 2 + 15) / 16 * 16;
     int64_t bytes = (int64_t)(p.H + 2) * o.pitch * nv * 16;
-    if (bytes <= kLdsPerCu) {
+    // one workgroup per (image, group) holds a CU for the whole image: with
+    // fewer of them than CUs (small batches), square tiles sized to fill the GPU
+    const bool fill = backward_fill_gpu() && (int64_t)p.N * p.G < kCus;
+    if (bytes <= kLdsPerCu && !fill) {
         o.th = p.Ho;
         o.tw = p.Wo;
         o.ry = o.rx = p.pad + 1;              // the window starts at pixel -1
@@ -294,6 +298,10 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
         // around it, points beyond read their corners from global memory.
         // DCNV4_BWD_OM="<th>,<tw>,<r>" overrides the shape (1..256, 0..64).
         int th = 32, tw = 32, r = 8;
+        if (fill) {
+            const double t = sqrt((double)p.Ho * p.Wo * p.N * p.G / kCus);
+            th = tw = t < 4.0 ? 4 : t > 32.0 ? 32 : (int)t;
+        }
         if (const char* env = getenv("DCNV4_BWD_OM")) {
             int eh = 0, ew = 0, er = -1;
             if (sscanf(env, "%d,%d,%d", &eh, &ew, &er) == 3 && eh >= 1 && eh <= 256 && ew >= 1 && ew <= 256 &&
@@ -313,7 +321,9 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
         o.pitch = (o.ww + 15) / 16 * 16;
         bytes = (int64_t)o.wh * o.pitch * nv * 16;
         if (bytes > kLdsPerCu) return false;
-        o.block = 1024;
+        // enough waves for one pass over the tile's (unit, point) lanes
+        const int64_t waves = ((int64_t)o.th * o.tw + (64 / p.P) - 1) / (64 / p.P);
+        o.block = (int)(waves < 16 ? waves * 64 : 1024);
     }
     o.tiles_y = (p.Ho + o.th - 1) / o.th;
     o.tiles_x = (p.Wo + o.tw - 1) / o.tw;

@@ -44,6 +44,8 @@ struct Plan {
 
 // Largest LDS allocation one workgroup may use on gfx950 (the CU's 160 KiB).
 constexpr int kLdsPerCu = 160 * 1024;
+// Compute units of an MI355X: a grid with fewer workgroups leaves CUs idle.
+constexpr int kCus = 256;
 
 // Pure host: pick the kernel and launch shape for a validated problem.
 void make_plan(const Problem& p, Plan* plan);
@@ -60,6 +62,9 @@ int backward_x_chunk(const Problem& p);
 // When the whole image does not fit: the tiled LDS x-gradient kernel's
 // channels per workgroup, log2 tile side and margin (false: global atomics).
 bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin);
+// Whether the backward's planners replace whole-image kernels whose grid
+// cannot fill the GPU by tiled ones (environment DCNV4_BWD_FILL=0: no).
+bool backward_fill_gpu();
 // Launch shape of the offset/weight-gradient LDS kernel: output tiles of
 // th x tw units (the whole image when its bordered copy fits), windows of
 // wh x ww pixels from ry / rx pixels before a tile's grid, rows of `pitch`

@@ -135,7 +135,7 @@ bool plan_window(const Problem& p, Plan* pl)
     // units of three or more vectors: one lane per vector (whole-unit lanes
     // need so many registers that a workgroup is capped at 512 threads)
     int lpu = (t.split == 1 && nv > 1) || (t.split < 0 && nv >= 3) ? nv : 1;
-    const int cus = 256;
+    const int cus = kCus;
 
     // group blocks to try, smallest first (all divisors of G unless tuned)
     int order[64], no = 0;

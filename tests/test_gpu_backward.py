@@ -35,6 +35,18 @@ def _gpu():
     yield
 
 
+@pytest.fixture(params=["fill", "whole"], autouse=True)
+def plan_mode(request, monkeypatch):
+    """Every test twice: with the planner's own choice (batches too small to
+    fill the GPU with whole-image workgroups take tiles) and with the
+    whole-image kernels kept wherever they fit (DCNV4_BWD_FILL=0)."""
+    if request.param == "whole":
+        monkeypatch.setenv("DCNV4_BWD_FILL", "0")
+    else:
+        monkeypatch.delenv("DCNV4_BWD_FILL", raising=False)
+    return request.param
+
+
 def f64(a, dtype):
     return ref.to_f32(a, dtype).astype(np.float64)
 
