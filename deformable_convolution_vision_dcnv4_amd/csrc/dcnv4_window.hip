@@ -114,6 +114,22 @@ __device__ __forceinline__ void pin(PointRegs<NV>& r)
     }
 }
 
+// Index of the n-th (from 0) set bit of m; n < popcount(m).
+__device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, int n)
+{
+    uint32_t pos = 0;
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+        const int c = __popcll(m & ((1ull << w) - 1));
+        if (n >= c) {
+            n -= c;
+            m >>= w;
+            pos += w;
+        }
+    }
+    return pos;
+}
+
 // Per-workgroup constants the point steps need.
 struct WinCtx {
     const char* lbase;
@@ -571,11 +587,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     }
 
     if (!FULL) {
-        while (fbmask) {
-            const uint32_t pass = (uint32_t)__builtin_ctzll(fbmask);
-            fbmask &= fbmask - 1;
+        // the wave's fallback items (item threadIdx.x + pass * B for bit
+        // `pass` of a lane's fbmask), packed densely over its 64 lanes: a
+        // batch of 64 costs one round of global reads, where each lane's own
+        // items would cost a round per pass holding any of them
+        auto fallback_item = [&](uint32_t it) {
             int oy, ox, gl;
-            const uint32_t it = threadIdx.x + pass * B;
             unit_of(unit_of_item(it), oy, ox, gl);
             const uint32_t vb = SPLIT ? (it - unit_of_item(it) * lpu) * 16u : 0u;   // this lane's vector
             const int g = g0 + gl;
@@ -593,6 +610,27 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 #pragma unroll
             for (int v = 0; v < NV; ++v)
                 *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
+        };
+        const uint32_t npass = (items + B - 1) / B;
+        const uint32_t wbase = threadIdx.x - lane;   // the wave's first thread
+        uint32_t p = 0;                              // pass of the items in mp
+        uint64_t mp = __ballot((int)(fbmask & 1u));  // its items not yet given out
+        for (;;) {
+            // a batch: lanes 0 .. fill - 1 take the next items, pass by pass
+            int fill = 0;
+            int my = -1;
+            while (fill < 64) {
+                while (!mp && ++p < npass) mp = __ballot((int)((fbmask >> p) & 1u));
+                if (!mp) break;
+                const int cnt = __popcll(mp);
+                const int take = min(cnt, 64 - fill);
+                const int nth = (int)lane - fill;
+                if (nth >= 0 && nth < take) my = (int)(wbase + nth_set_bit(mp, nth) + p * B);
+                mp = take < cnt ? mp & (~0ull << nth_set_bit(mp, take)) : 0ull;
+                fill += take;
+            }
+            if (!fill) break;
+            if (my >= 0) fallback_item((uint32_t)my);
         }
     }
 }
