@@ -54,6 +54,7 @@ PATHS = [
     ("window_bands", 2, 60, 60, 1, 16, 8.0, ("f32",), "window", 0, "kernel=window"),
     ("window_bands16", 2, 60, 60, 2, 32, 6.0, ("f16", "bf16"), "window", 0, "kernel=window"),
     ("window_fill_bands", 16, 28, 24, 4, 16, 2.0, ("f16",), "window", 0, ""),
+    ("window_coal_bands_fallback", 2, 60, 60, 1, 16, 8.0, ("f16", "bf16"), "window", 0, "kernel=window,full=0"),
     ("direct", 2, 12, 13, 4, 6, 2.0, ("f32", "f16", "bf16"), "direct", 0, ""),
     ("direct_small_batch", 2, 12, 13, 4, 16, 2.0, ("f32", "f16"), "direct", 0, ""),
 ]
