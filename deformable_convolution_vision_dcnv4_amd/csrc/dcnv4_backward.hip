@@ -15,13 +15,20 @@
 // the corners floor(p), floor(p)+1 the forward uses).  Points the forward
 // skips get zero gradient.
 //
-// Layout of the work: as the forward's direct kernel, lanes take (unit,
+// Kernels here: k_backward, the general one (any K, any width), and for K = 3
+// x's gradient in LDS, k_backward_x (a channel chunk of the whole bordered
+// image) or k_backward_x_tiled (64 x 64 down to 8 x 8 tiles, for images too
+// large for LDS or batches too small to fill the GPU); the offset and weight
+// gradients of K = 3 come from the LDS-window kernel of
+// dcnv4_backward_window.hip when it applies.
+//
+// k_backward's layout: as the forward's direct kernel, lanes take (unit,
 // vector) pairs, unit = (pixel, group), L = Cg*s/VB lanes per unit, the L
 // lanes of a unit in one wave.  Per point, each lane forms its channels'
 // partial sums; the unit's first lane adds the L partials in lane order (a
 // fixed order: the offset and weight gradients are reproducible) and writes
-// them.  x's gradient is a scatter: hardware fp32 atomic adds into a buffer
-// this library zeroes first (its summation order is not fixed).
+// them.  Its x's gradient (other K) is a scatter: hardware fp32 atomic adds
+// into a buffer this library zeroes first (summation order not fixed).
 
 #include <stdio.h>
 #include <stdlib.h>

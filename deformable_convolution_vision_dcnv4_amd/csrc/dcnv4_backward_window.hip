@@ -14,13 +14,16 @@
 // products per point instead of three sums of bilinear expressions per
 // channel).  Points the forward skips get zero gradients.
 //
-// Work layout: one workgroup = (image n, group g); the whole zero-bordered
-// image of that group, [-1, H] x [-1, W], is copied to LDS (one plane per
-// 16-byte channel vector, rows of `pitch` entries, the columns past W + 1
-// zero), so every corner of every point is read from LDS.  One lane = one
-// (unit, point) with all of the group's channels.  Workgroups are renumbered
-// per XCD so that an image's groups, whose rows share cache lines, meet in
-// one L2.  The results are deterministic (a fixed operation order).
+// Work layout: one workgroup = (image n, output tile, group g).  A window of
+// the zero-bordered image of that group is copied to LDS (one plane per
+// 16-byte channel vector, rows of `pitch` entries): the whole image,
+// [-1, H] x [-1, W], when it fits and the batch fills the GPU (one tile per
+// image: every corner of every point is then in LDS), else the tile's grid
+// with a margin, and a point whose corners leave the window reads them from
+// global memory.  One lane = one (unit, point) with all of the group's
+// channels.  Workgroups are renumbered per XCD so that a tile's groups, whose
+// pixels share cache lines, meet in one L2.  The results are deterministic
+// (a fixed operation order, whichever memory a corner comes from).
 
 #include <math.h>
 #include <stdio.h>

@@ -179,9 +179,9 @@ bool plan_window(const Problem& p, Plan* pl)
         GB = gb; TW = t.tw ? t.tw : p.Wo;
     }
     // tiles of 16 x 64 outputs with a 12-pixel margin, one lane per vector,
-    // when rows are too wide for bands (the 256x256 shape: 11% faster than
-    // the direct kernel with its 8-pixel offsets; smaller offsets fall back
-    // less)
+    // when rows are too wide for bands (the 256x256 shape: 126 against 179 us
+    // for the direct kernel with its 8-pixel offsets, which send a third of
+    // the units to the fallback; smaller offsets fall back less)
     if (!GB && t.full != 1 && nv >= 2) {
         const int R2 = t.r >= 0 ? t.r : 12;
         const int th = t.th ? t.th : 16, tw = t.tw ? t.tw : 64;
