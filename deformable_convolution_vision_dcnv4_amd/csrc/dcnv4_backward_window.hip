@@ -193,44 +193,56 @@ __global__ void __launch_bounds__(1024) k_backward_om_window(BArgs a, uint32_t t
         // entry 0 (a valid one then reads its corners from global memory,
         // a skipped one's gradients are zero whatever it reads)
         const int a00 = (valid & inwin) ? (y0 - wy0) * row16 + ((x0 - wx0) << 4) : 0;
-        u32x4 cv[NV][4];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const char* p0 = lbase + a00 + v * plane;
-            cv[v][0] = *reinterpret_cast<const u32x4*>(p0);
-            cv[v][1] = *reinterpret_cast<const u32x4*>(p0 + 16);
-            cv[v][2] = *reinterpret_cast<const u32x4*>(p0 + row16);
-            cv[v][3] = *reinterpret_cast<const u32x4*>(p0 + row16 + 16);
-        }
-        if (valid & !inwin) {
-            // corners from global memory, zero off the image
-            const bool iny0 = y0 >= 0, iny1 = y0 + 1 < a.H, inx0 = x0 >= 0, inx1 = x0 + 1 < a.W;
-            const uint32_t base = (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + grp_bytes;
-            const uint32_t off[4] = {(iny0 & inx0) ? base : kOobOffset,
-                                     (iny0 & inx1) ? base + pix_bytes : kOobOffset,
-                                     (iny1 & inx0) ? base + row_bytes : kOobOffset,
-                                     (iny1 & inx1) ? base + row_bytes + pix_bytes : kOobOffset};
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-#pragma unroll
-                for (int cr = 0; cr < 4; ++cr)
-                    cv[v][cr] = buf_load16(rx, off[cr] == kOobOffset ? kOobOffset : off[cr] + 16u * v);
-            }
-        }
+        // corners from global memory (zero off the image) when the point is
+        // valid but leaves the window
+        const bool glob = valid & !inwin;
+        const bool iny0 = y0 >= 0, iny1 = y0 + 1 < a.H, inx0 = x0 >= 0, inx1 = x0 + 1 < a.W;
+        const uint32_t gbase = (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + grp_bytes;
+        const uint32_t goffs[4] = {(iny0 & inx0) ? gbase : kOobOffset,
+                                   (iny0 & inx1) ? gbase + pix_bytes : kOobOffset,
+                                   (iny1 & inx0) ? gbase + row_bytes : kOobOffset,
+                                   (iny1 & inx1) ? gbase + row_bytes + pix_bytes : kOobOffset};
+        // vectors whose corners are held at once: all of them for units of
+        // one or two vectors, one at a time for wider units (registers)
+        constexpr int VC = NV <= 2 ? NV : 1;
         float A00 = 0.0f, A01 = 0.0f, A10 = 0.0f, A11 = 0.0f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            float gr[EPV];
-            const uint32_t w[4] = {gv[v].x, gv[v].y, gv[v].z, gv[v].w};
+        for (int v0 = 0; v0 < NV; v0 += VC) {
+            u32x4 cv[VC][4];
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                if constexpr (s == 4) gr[e] = __uint_as_float(w[e]);
-                else gr[e] = E::raw_to_f((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+            for (int j = 0; j < VC; ++j) {
+                const char* p0 = lbase + a00 + (v0 + j) * plane;
+                cv[j][0] = *reinterpret_cast<const u32x4*>(p0);
+                cv[j][1] = *reinterpret_cast<const u32x4*>(p0 + 16);
+                cv[j][2] = *reinterpret_cast<const u32x4*>(p0 + row16);
+                cv[j][3] = *reinterpret_cast<const u32x4*>(p0 + row16 + 16);
             }
-            A00 = dot_vec16<DT>(A00, gr, cv[v][0]);
-            A01 = dot_vec16<DT>(A01, gr, cv[v][1]);
-            A10 = dot_vec16<DT>(A10, gr, cv[v][2]);
-            A11 = dot_vec16<DT>(A11, gr, cv[v][3]);
+            if (glob) {
+#pragma unroll
+                for (int j = 0; j < VC; ++j) {
+#pragma unroll
+                    for (int cr = 0; cr < 4; ++cr)
+                        cv[j][cr] = buf_load16(rx, goffs[cr] == kOobOffset ? kOobOffset : goffs[cr] + 16u * (v0 + j));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < VC; ++j) {
+                float gr[EPV];
+                const u32x4 gvv = gv[v0 + j];
+                const uint32_t w[4] = {gvv.x, gvv.y, gvv.z, gvv.w};
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    if constexpr (s == 4) gr[e] = __uint_as_float(w[e]);
+                    else gr[e] = E::raw_to_f((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+                }
+                A00 = dot_vec16<DT>(A00, gr, cv[j][0]);
+                A01 = dot_vec16<DT>(A01, gr, cv[j][1]);
+                A10 = dot_vec16<DT>(A10, gr, cv[j][2]);
+                A11 = dot_vec16<DT>(A11, gr, cv[j][3]);
+            }
+            // wide units: the next vector's reads are not hoisted above these
+            // products (that would hold every vector's corners at once)
+            if constexpr (VC < NV) asm volatile("" ::: "memory");
         }
         float sm = (hy * hx) * A00;
         sm = fmaf(hy * lx, A01, sm);
@@ -266,6 +278,13 @@ hipError_t launch_nv(const BArgs& a, int nv, int block, uint32_t total, size_t l
     switch (nv) {
         case 1: launch_rc<DT, 1>(a, block, total, lds, stream); break;
         case 2: launch_rc<DT, 2>(a, block, total, lds, stream); break;
+        case 3: launch_rc<DT, 3>(a, block, total, lds, stream); break;
+        case 4:
+            if constexpr (DT != DCNV4_BF16) {
+                launch_rc<DT, 4>(a, block, total, lds, stream);
+                break;
+            }
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -278,7 +297,10 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
     const int s = p.dtype == DCNV4_F32 ? 4 : 2;
     if (p.K != 3 || (p.Cg * s) % 16) return false;
     const int nv = p.Cg * s / 16;
-    if (nv > 2) return false;
+    // units of up to four vectors (three in bf16, whose widening takes more
+    // registers): wider ones spilled, and the latent shape's five bf16
+    // vectors measured no faster than k_backward (138 us either way)
+    if (nv > (p.dtype == DCNV4_BF16 ? 3 : 4)) return false;
     if ((uintptr_t)p.x % 16 || (uintptr_t)gout % 16) return false;
     // the whole zero-bordered image when it fits, rows a whole number of
     // 16-entry bank groups apart (as the forward's windows)
@@ -300,7 +322,9 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
         // tiles of th x tw units; the window covers their grid and r pixels
         // around it, points beyond read their corners from global memory.
         // DCNV4_BWD_OM="<th>,<tw>,<r>" overrides the shape (1..256, 0..64).
+        // Units wider than the LDS allows at 32 x 32 take smaller square tiles.
         int th = 32, tw = 32, r = 8;
+        bool shrink = true;
         if (fill) {
             const double t = sqrt((double)p.Ho * p.Wo * p.N * p.G / kCus);
             th = tw = t < 4.0 ? 4 : t > 32.0 ? 32 : (int)t;
@@ -312,18 +336,24 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
                 th = eh;
                 tw = ew;
                 r = er;
+                shrink = false;
             }
         }
-        o.th = th < p.Ho ? th : p.Ho;
-        o.tw = tw < p.Wo ? tw : p.Wo;
-        o.ry = o.rx = r;
-        const int64_t eh = (int64_t)(o.th - 1) * p.stride + 2 * p.dil + 2 + 2 * r;
-        const int64_t ew = (int64_t)(o.tw - 1) * p.stride + 2 * p.dil + 2 + 2 * r;
-        o.wh = (int)(eh < p.H + 2 ? eh : p.H + 2);
-        o.ww = (int)(ew < p.W + 2 ? ew : p.W + 2);
-        o.pitch = (o.ww + 15) / 16 * 16;
-        bytes = (int64_t)o.wh * o.pitch * nv * 16;
-        if (bytes > kLdsPerCu) return false;
+        for (;;) {
+            o.th = th < p.Ho ? th : p.Ho;
+            o.tw = tw < p.Wo ? tw : p.Wo;
+            o.ry = o.rx = r;
+            const int64_t eh = (int64_t)(o.th - 1) * p.stride + 2 * p.dil + 2 + 2 * r;
+            const int64_t ew = (int64_t)(o.tw - 1) * p.stride + 2 * p.dil + 2 + 2 * r;
+            o.wh = (int)(eh < p.H + 2 ? eh : p.H + 2);
+            o.ww = (int)(ew < p.W + 2 ? ew : p.W + 2);
+            o.pitch = (o.ww + 15) / 16 * 16;
+            bytes = (int64_t)o.wh * o.pitch * nv * 16;
+            if (bytes <= kLdsPerCu) break;
+            if (!shrink || (th <= 4 && tw <= 4)) return false;
+            th = th * 3 / 4 > 4 ? th * 3 / 4 : 4;
+            tw = tw * 3 / 4 > 4 ? tw * 3 / 4 : 4;
+        }
         // enough waves for one pass over the tile's (unit, point) lanes
         const int64_t waves = ((int64_t)o.th * o.tw + (64 / p.P) - 1) / (64 / p.P);
         o.block = (int)(waves < 16 ? waves * 64 : 1024);

@@ -75,8 +75,9 @@ struct OmPlan {
     size_t lds;
 };
 // Whether the offset/weight gradients can read their corners from an LDS
-// window of each (image, group) (K = 3, one or two 16-byte vectors per unit,
-// 16-byte aligned x and output gradient, a window that fits the LDS), and how.
+// window of each (image, tile, group) (K = 3, one to five 16-byte vectors per
+// unit, 16-byte aligned x and output gradient, a window that fits the LDS),
+// and how.
 bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan);
 hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
                            hipStream_t stream);

@@ -112,7 +112,7 @@ struct BArgs {
 hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hipStream_t stream);
 // Offset/weight gradients with a window of each (image, tile, group) in LDS
 // (the tile shape in a.om_*): N * tiles * G workgroups of `block` threads,
-// `lds` bytes of window, 16-byte vectors per unit nv (1 or 2).
+// `lds` bytes of window, 16-byte vectors per unit nv (1 to 4; 1 to 3 in bf16).
 hipError_t launch_backward_om_window(const BArgs& a, int dtype, int nv, int block, size_t lds,
                                      hipStream_t stream);
 hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);

@@ -118,6 +118,11 @@ for dtype in ("f32", "f16", "bf16"):
     for Cg in (16, 6, 40):
         CASES.append((Workload("bwd", 2, 11, 13, 3, Cg, (dtype,), offset_dist=("normal", 2.0),
                                mask_dist=("normal", 0.7), seed=43), dtype))
+# units of three and four 16-byte vectors in 16-bit types (the offset/weight
+# window kernel's wider variants; five bf16 vectors take the general kernel)
+for dtype, Cg in (("f16", 24), ("f16", 32), ("bf16", 24)):
+    CASES.append((Workload("bwd", 2, 11, 13, 3, Cg, (dtype,), offset_dist=("normal", 2.0),
+                           mask_dist=("normal", 0.7), seed=43), dtype))
 for K, s, p, d, rc in ((5, 1, 2, 1, False), (3, 2, 1, 1, False), (3, 1, 2, 2, False), (3, 1, 1, 1, True),
                        (1, 1, 0, 1, False)):
     CASES.append((Workload("bwd_geom", 2, 12, 10, 2, 8, ("f32",), offset_dist=("normal", 1.5), K=K, stride=s,
