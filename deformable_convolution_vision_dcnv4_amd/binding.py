@@ -19,8 +19,9 @@ F32, F16, BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 # Every symbol include/dcnv4.h declares.
-EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_forward_softmax", "dcnv4_backward", "dcnv4_output_dim", "dcnv4_status_string",
-           "dcnv4_last_error", "dcnv4_version", "dcnv4_query_plan", "dcnv4_kernel_name")
+EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_forward_softmax", "dcnv4_backward", "dcnv4_output_dim",
+           "dcnv4_status_string", "dcnv4_last_error", "dcnv4_version", "dcnv4_query_plan",
+           "dcnv4_query_backward_plan", "dcnv4_kernel_name")
 
 
 class Plan(ctypes.Structure):
@@ -34,6 +35,21 @@ class Plan(ctypes.Structure):
     def as_dict(self):
         d = {name: getattr(self, name) for name, _ in self._fields_}
         d["kernel"] = lib().dcnv4_kernel_name(self.kernel).decode()
+        return d
+
+
+class BackwardPlan(ctypes.Structure):
+    _fields_ = [("x_path", ctypes.c_int), ("x_channels", ctypes.c_int), ("x_tile", ctypes.c_int),
+                ("x_margin", ctypes.c_int), ("x_lds_bytes", ctypes.c_int), ("om_path", ctypes.c_int),
+                ("om_tile_h", ctypes.c_int), ("om_tile_w", ctypes.c_int), ("om_lds_bytes", ctypes.c_int)]
+
+    X_PATHS = ("none", "lds_whole", "lds_tiles", "atomics")
+    OM_PATHS = ("none", "lds_window", "global")
+
+    def as_dict(self):
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["x_path"] = self.X_PATHS[self.x_path]
+        d["om_path"] = self.OM_PATHS[self.om_path]
         return d
 
 
@@ -71,6 +87,9 @@ def lib():
         L.dcnv4_query_plan.argtypes = [vp, vp, vp, vp] + [i32] * 9 + [f32, i32, i64, i64, i32,
                                                                        ctypes.POINTER(Plan)]
         L.dcnv4_query_plan.restype = i32
+        L.dcnv4_query_backward_plan.argtypes = [vp] * 4 + [i32] * 11 + [f32, i32, i64, i64, i32,
+                                                                          ctypes.POINTER(BackwardPlan)]
+        L.dcnv4_query_backward_plan.restype = i32
         L.dcnv4_kernel_name.argtypes = [i32]
         L.dcnv4_kernel_name.restype = ctypes.c_char_p
         _lib = L
@@ -249,4 +268,19 @@ def query_plan(x, offset, mask, out, *, kernel_size=3, stride=1, pad=1, dilation
                                   stride, pad, dilation, float(offset_scale),
                                   1 if remove_center else 0, orow, mrow, _DTYPE_CODE[x.dtype],
                                   ctypes.byref(pl)))
+    return pl.as_dict()
+
+
+def query_backward_plan(x, offset, mask, grad_out, *, kernel_size=3, stride=1, pad=1, dilation=1,
+                        offset_scale=1.0, remove_center=False, group=None, need=("x", "offset", "mask")):
+    """The kernels the backward picks for these tensors (host only)."""
+    N, H, W, C, G, K, P = _prepare(x, offset, mask, kernel_size, remove_center, group, None)
+    optr, orow = _row_view(offset, "offset")
+    mptr, mrow = _row_view(mask, "mask")
+    pl = BackwardPlan()
+    _check(lib().dcnv4_query_backward_plan(x.data_ptr(), optr, mptr, grad_out.data_ptr(), int("x" in need),
+                                           int("offset" in need or "mask" in need), N, H, W, G, C // G, K,
+                                           stride, pad, dilation, float(offset_scale),
+                                           1 if remove_center else 0, orow, mrow, _DTYPE_CODE[x.dtype],
+                                           ctypes.byref(pl)))
     return pl.as_dict()

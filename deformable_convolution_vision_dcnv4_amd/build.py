@@ -6,6 +6,7 @@ Flags: contraction off (the binary32 operation order is part of the
 operator's contract), packed-fp32 instructions disabled, -O3.
 """
 import argparse
+import concurrent.futures
 import glob
 import hashlib
 import os
@@ -47,11 +48,26 @@ def hipcc():
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
-def build(verbose=False, asm_dir=None):
-    cmd = [hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-shared", "-o", LIB + ".tmp"] + sources()
+def build(verbose=False, asm_dir=None, jobs=None):
+    """Compile every source to an object in parallel (one hipcc per file),
+    then link the shared library."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".o")) for src in sources()]
+    cmds = [[hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
+            for src, obj in zip(sources(), objs)]
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        for cmd, r in zip(cmds, ex.map(lambda c: subprocess.run(c, cwd=CSRC, capture_output=True, text=True),
+                                       cmds)):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{r.stderr}")
+    link = [hipcc()] + HIP_FLAGS + ["-shared", "-o", LIB + ".tmp"] + objs
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, cwd=CSRC)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True, cwd=CSRC)
     os.replace(LIB + ".tmp", LIB)
     if asm_dir:
         # device ISA of each source, for inspection

@@ -232,6 +232,14 @@ __global__ void __launch_bounds__(256) k_backward(BArgs a, uint32_t total_blocks
 // do not depend on the order of the adds, so x's gradient is reproducible;
 // each term is off by at most 2^-(F+1).  An (image, group) whose weights or
 // output gradient hold a non-finite value uses binary32 LDS atomic adds.
+// Static LDS of the x-gradient kernels: per-wave maxima and non-finite flags
+// of a 1024-thread workgroup.  The planners reserve kBwdXStaticLds for it.
+struct BxShared {
+    float red[2][16];
+    bool flag[16];
+};
+static_assert(sizeof(BxShared) <= kBwdXStaticLds, "static LDS of the x-gradient kernels");
+
 template <int DT, int RC, int CC>
 __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blocks, uint32_t per_xcd)
 {
@@ -239,8 +247,9 @@ __global__ void __launch_bounds__(1024) k_backward_x(BArgs a, uint32_t total_blo
     constexpr int s = E::kBytes;
     constexpr int P = 9 - RC;                 // K = 3
     extern __shared__ unsigned long long acc[];
-    __shared__ float red[2][16];
-    __shared__ bool flag[16];
+    __shared__ BxShared sh_;
+    float (&red)[2][16] = sh_.red;
+    bool (&flag)[16] = sh_.flag;
     const int chunks = a.Cg / CC;
     // renumbered so that each XCD runs a contiguous range: the groups of an
     // image, whose rows share cache lines, meet in one L2
@@ -425,8 +434,9 @@ __global__ void __launch_bounds__(1024) k_backward_x_tiled(BArgs a, uint32_t tot
     constexpr int s = E::kBytes;
     constexpr int P = 9 - RC;                 // K = 3
     extern __shared__ unsigned long long acc[];
-    __shared__ float red[2][16];
-    __shared__ bool flag[16];
+    __shared__ BxShared sh_;
+    float (&red)[2][16] = sh_.red;
+    bool (&flag)[16] = sh_.flag;
     const int chunks = a.Cg / CC;
     uint32_t b;
     if (!logical_block(blockIdx.x, total_blocks, per_xcd, &b)) return;
@@ -688,6 +698,38 @@ int backward_vec_bytes(const Problem& p, const void* gout)
     return vb;
 }
 
+void plan_backward(const Problem& p, const void* gout, bool want_x, bool want_om, BwdPlan* bp)
+{
+    memset(bp, 0, sizeof *bp);
+    // x's gradient in LDS when a channel chunk of the bordered image fits,
+    // else in LDS tiles (K = 3), else with global atomics only
+    int cc = want_x ? backward_x_chunk(p) : 0;
+    // one workgroup per (image, group, chunk) holds a CU for the whole
+    // image: with at most a quarter as many of them as CUs (small batches),
+    // tiles fill the GPU.  Tiles add visits of the units around them, which
+    // measured slower than the whole image with a third of the CUs busy (the
+    // latent shape at batch 1: 103 against 94 us) and faster with a quarter
+    // (stage-1 shape at batch 4: 50 against 62 us)
+    if (cc && backward_fill_gpu() && (int64_t)p.N * p.G * (p.Cg / cc) * 4 <= p.cus) cc = 0;
+    if (!want_x) {
+        bp->x_path = 0;
+    } else if (cc) {
+        bp->x_path = 1;
+        bp->cc = cc;
+        bp->x_lds = (int)((int64_t)(p.H + 2) * (p.W + 2) * cc * 8) + kBwdXStaticLds;
+    } else if (backward_x_tiles(p, &bp->cc, &bp->tile_sh, &bp->margin)) {
+        bp->x_path = 2;
+        bp->x_lds = (int)(((int64_t)1 << (2 * bp->tile_sh)) * bp->cc * 8) + kBwdXStaticLds;
+    } else {
+        bp->x_path = 3;
+    }
+    // offset and weight gradients from an LDS copy of each (image, group)
+    // when it fits, unless x's gradient needs the atomics kernel anyway
+    if (!want_om) bp->om_path = 0;
+    else if (bp->x_path != 3 && backward_om_window_plan(p, gout, &bp->om)) bp->om_path = 1;
+    else bp->om_path = 2;
+}
+
 hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
                            hipStream_t stream)
 {
@@ -718,18 +760,12 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
     a.div_G = make_fastdiv((uint32_t)p.G);
     a.div_Wo = make_fastdiv((uint32_t)p.Wo);
 
-    // x's gradient in LDS when a channel chunk of the bordered image fits,
-    // else in LDS tiles (K = 3), else with global atomics only
-    a.cc = gx ? backward_x_chunk(p) : 0;
-    // one workgroup per (image, group, chunk) holds a CU for the whole
-    // image: with at most a quarter as many of them as CUs (small batches),
-    // tiles fill the GPU.  Tiles add visits of the units around them, which
-    // measured slower than the whole image with a third of the CUs busy (the
-    // latent shape at batch 1: 103 against 94 us) and faster with a quarter
-    // (stage-1 shape at batch 4: 50 against 62 us)
-    if (a.cc && backward_fill_gpu() && (int64_t)p.N * p.G * (p.Cg / a.cc) * 4 <= kCus) a.cc = 0;
-    const bool whole = a.cc > 0;
-    const bool tiled = gx && !whole && backward_x_tiles(p, &a.cc, &a.tile_sh, &a.margin);
+    BwdPlan bp;
+    plan_backward(p, gout, gx != nullptr, goff || gmask, &bp);
+    const bool whole = bp.x_path == 1, tiled = bp.x_path == 2;
+    a.cc = bp.cc;
+    a.tile_sh = bp.tile_sh;
+    a.margin = bp.margin;
     if (tiled) {
         a.tiles_y = (p.H + (1 << a.tile_sh) - 1) >> a.tile_sh;
         a.tiles_x = (p.W + (1 << a.tile_sh) - 1) >> a.tile_sh;
@@ -741,11 +777,9 @@ hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float*
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // offset and weight gradients from an LDS copy of each (image, group)
-    // when it fits, unless x's gradient needs the atomics kernel anyway
-    OmPlan om;
-    const bool om_window = (goff || gmask) && (whole || tiled || !gx) && backward_om_window_plan(p, gout, &om);
+    const bool om_window = bp.om_path == 1;
     if (om_window) {
+        const OmPlan& om = bp.om;
         BArgs b = a;
         b.gx = nullptr;
         b.pitch = om.pitch;
@@ -813,9 +847,9 @@ bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin)
     if (backward_fill_gpu()) {
         for (; sh > 3; --sh) {
             int c = 16;
-            while (c > 1 && (p.Cg % c || ((int64_t)8 << (2 * sh)) * c > kLdsPerCu)) c /= 2;
+            while (c > 1 && (p.Cg % c || ((int64_t)8 << (2 * sh)) * c + kBwdXStaticLds > kLdsPerCu)) c /= 2;
             const int64_t tiles = (int64_t)((p.H + (1 << sh) - 1) >> sh) * ((p.W + (1 << sh) - 1) >> sh);
-            if ((int64_t)p.N * tiles * p.G * (p.Cg / c) >= kCus) break;
+            if ((int64_t)p.N * tiles * p.G * (p.Cg / c) >= p.cus) break;
         }
     }
     // DCNV4_BWD_TILE="<log2 side>,<margin>" overrides both (side 8 to 128, margin 0 to 256)
@@ -828,7 +862,7 @@ bool backward_x_tiles(const Problem& p, int* cc, int* tile_sh, int* margin)
     }
     const int64_t cell = ((int64_t)1 << (2 * sh)) * 8;
     for (int c = 16; c >= 1; c /= 2) {
-        if (p.Cg % c == 0 && cell * c <= kLdsPerCu) {
+        if (p.Cg % c == 0 && cell * c + kBwdXStaticLds <= kLdsPerCu) {
             *cc = c;
             *tile_sh = sh;
             *margin = m;
@@ -848,11 +882,12 @@ bool backward_fill_gpu()
 int backward_x_chunk(const Problem& p)
 {
     // K = 3: the most channels (a power of two dividing Cg, at most 16) whose
-    // bordered image of 64-bit accumulators fits in LDS
+    // bordered image of 64-bit accumulators fits in LDS beside the kernel's
+    // static LDS
     if (p.K != 3) return 0;
     const int64_t cell = (int64_t)(p.H + 2) * (p.W + 2) * 8;
     for (int cc = 16; cc >= 1; cc /= 2)
-        if (p.Cg % cc == 0 && cell * cc <= kLdsPerCu) return cc;
+        if (p.Cg % cc == 0 && cell * cc + kBwdXStaticLds <= kLdsPerCu) return cc;
     return 0;
 }
 

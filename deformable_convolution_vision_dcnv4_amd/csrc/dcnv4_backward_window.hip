@@ -309,7 +309,7 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
     int64_t bytes = (int64_t)(p.H + 2) * o.pitch * nv * 16;
     // one workgroup per (image, group) holds a CU for the whole image: with
     // fewer of them than CUs (small batches), square tiles sized to fill the GPU
-    const bool fill = backward_fill_gpu() && (int64_t)p.N * p.G < kCus;
+    const bool fill = backward_fill_gpu() && (int64_t)p.N * p.G < p.cus;
     if (bytes <= kLdsPerCu && !fill) {
         o.th = p.Ho;
         o.tw = p.Wo;
@@ -326,7 +326,7 @@ bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan)
         int th = 32, tw = 32, r = 8;
         bool shrink = true;
         if (fill) {
-            const double t = sqrt((double)p.Ho * p.Wo * p.N * p.G / kCus);
+            const double t = sqrt((double)p.Ho * p.Wo * p.N * p.G / p.cus);
             th = tw = t < 4.0 ? 4 : t > 32.0 ? 32 : (int)t;
         }
         if (const char* env = getenv("DCNV4_BWD_OM")) {

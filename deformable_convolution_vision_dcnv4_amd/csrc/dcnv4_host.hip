@@ -2,10 +2,12 @@
 //
 // Every argument is checked on the host before the first HIP call, so an
 // invalid call launches nothing and writes nothing.  The only global state is
-// a per-device cache of "is this a gfx950 device", filled on first use.
+// a per-device cache of "is this a gfx950 device" and its compute-unit count,
+// filled on first use.
 
 #include <math.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -44,6 +46,18 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
 {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Compute units the planners size their grids for: DCNV4_CUS (1..4096) when
+// set (tests of the planners; a partitioned device), else the device's count,
+// else (plan queries, which make no HIP call) an MI355X's 256.
+int planner_cus(int device_cus)
+{
+    if (const char* e = getenv("DCNV4_CUS")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= 4096) return v;
+    }
+    return device_cus > 0 ? device_cus : dcnv4::kDefaultCus;
 }
 
 // Validate and fill a Problem.  Returns DCNV4_OK or an error status.  With
@@ -103,6 +117,7 @@ int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* m
     p->stride = stride; p->pad = pad; p->dil = dil; p->Ho = Ho; p->Wo = Wo;
     p->remove_center = remove_center; p->softmax = 0; p->off_row = offset_row; p->mask_row = mask_row;
     p->offset_scale = offset_scale; p->dtype = dtype;
+    p->cus = planner_cus(0);
     if (N == 0 || !check_pointers) return DCNV4_OK;
 
     if (!x || !offset || !mask || !out)
@@ -121,11 +136,13 @@ int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* m
     return DCNV4_OK;
 }
 
-// Is the current device a gfx950?  Cached per device id.
-int check_device()
+// Is the current device a gfx950?  Cached per device id, with its compute
+// unit count (multiProcessorCount), returned in *cus.
+int check_device(int* cus)
 {
     static std::mutex mu;
     static int cache[64];   // 0 unknown, 1 yes, 2 no
+    static int cu_count[64];
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -139,12 +156,14 @@ int check_device()
         if (e != hipSuccess)
             return fail(DCNV4_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
         cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        cu_count[dev] = prop.multiProcessorCount;
         if (cache[dev] == 2)
             return fail(DCNV4_ERR_HIP, "device %d is %s; this library is built for gfx950", dev,
                         prop.gcnArchName);
     }
     if (cache[dev] != 1)
         return fail(DCNV4_ERR_HIP, "device %d is not a gfx950", dev);
+    *cus = cu_count[dev];
     return DCNV4_OK;
 }
 
@@ -158,8 +177,10 @@ int forward_impl(const void* x, const void* offset, const void* mask, void* out,
                       offset_scale, remove_center, offset_row, mask_row, dtype);
     p.softmax = softmax;
     if (st != DCNV4_OK || N == 0) return st;
-    st = check_device();
+    int cus = 0;
+    st = check_device(&cus);
     if (st != DCNV4_OK) return st;
+    p.cus = planner_cus(cus);
     dcnv4::Plan plan;
     dcnv4::make_plan(p, &plan);
     const hipError_t e = dcnv4::launch_forward(p, plan, (hipStream_t)stream);
@@ -217,8 +238,10 @@ int backward_impl(const void* x, const void* offset, const void* mask, const voi
                    (grad_mask && overlaps(grad_x, gxb, grad_mask, gmb))))
         return fail(DCNV4_ERR_ALIAS, "grad_x overlaps grad_offset or grad_mask");
     if (!grad_x && !grad_offset && !grad_mask) return DCNV4_OK;
-    st = check_device();
+    int cus = 0;
+    st = check_device(&cus);
     if (st != DCNV4_OK) return st;
+    p.cus = planner_cus(cus);
     const hipError_t e = dcnv4::launch_backward(p, grad_out, grad_x, grad_offset, grad_mask, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DCNV4_ERR_HIP, "launch of the backward failed: %s", hipGetErrorString(e));
     return DCNV4_OK;
@@ -322,6 +345,35 @@ int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const 
     plan->full_window = pl.full;
     plan->lds_bytes = pl.lds_total;
     plan->coalesced_offsets = pl.coal;
+    return DCNV4_OK;
+}
+
+int dcnv4_query_backward_plan(const void* x, const void* offset, const void* mask, const void* grad_out,
+                              int need_x, int need_offset_or_mask,
+                              int N, int H, int W, int G, int Cg,
+                              int K, int stride, int pad, int dilation, float offset_scale,
+                              int remove_center, int64_t offset_row, int64_t mask_row,
+                              int dtype, dcnv4_backward_plan* plan)
+{
+    if (!plan) return fail(DCNV4_ERR_NULL, "plan is null");
+    dcnv4::Problem p;
+    const int st = validate(&p, x, offset, mask, nullptr, N, H, W, G, Cg, K, stride, pad, dilation,
+                            offset_scale, remove_center, offset_row, mask_row, dtype, false);
+    if (st != DCNV4_OK) return st;
+    dcnv4::BwdPlan bp;
+    dcnv4::plan_backward(p, grad_out, need_x != 0, need_offset_or_mask != 0, &bp);
+    memset(plan, 0, sizeof *plan);
+    plan->x_path = bp.x_path;
+    plan->x_channels = bp.cc;
+    plan->x_tile = bp.x_path == 2 ? 1 << bp.tile_sh : 0;
+    plan->x_margin = bp.x_path == 2 ? bp.margin : 0;
+    plan->x_lds_bytes = bp.x_lds;
+    plan->om_path = bp.om_path;
+    if (bp.om_path == 1) {
+        plan->om_tile_h = bp.om.th;
+        plan->om_tile_w = bp.om.tw;
+        plan->om_lds_bytes = (int)bp.om.lds;
+    }
     return DCNV4_OK;
 }
 

@@ -20,6 +20,7 @@ struct Problem {
     int64_t off_row, mask_row;
     float offset_scale;
     int dtype;
+    int cus;                // compute units the planners size grids for
 };
 
 enum KernelId {
@@ -44,8 +45,13 @@ struct Plan {
 
 // Largest LDS allocation one workgroup may use on gfx950 (the CU's 160 KiB).
 constexpr int kLdsPerCu = 160 * 1024;
-// Compute units of an MI355X: a grid with fewer workgroups leaves CUs idle.
-constexpr int kCus = 256;
+// Compute units of an MI355X, the planners' count when the device's is not
+// known (plan queries make no HIP call).
+constexpr int kDefaultCus = 256;
+// Static LDS of the x-gradient LDS kernels (per-wave maxima and non-finite
+// flags of a 1024-thread workgroup, rounded up): a workgroup's dynamic
+// accumulator plane plus this must fit in kLdsPerCu.
+constexpr int kBwdXStaticLds = 256;
 
 // Pure host: pick the kernel and launch shape for a validated problem.
 void make_plan(const Problem& p, Plan* plan);
@@ -79,6 +85,15 @@ struct OmPlan {
 // unit, 16-byte aligned x and output gradient, a window that fits the LDS),
 // and how.
 bool backward_om_window_plan(const Problem& p, const void* gout, OmPlan* plan);
+// What the backward launches for a problem (pure host).  x_path: 0 no x
+// gradient, 1 whole-image LDS kernel, 2 tiled LDS kernel, 3 global atomics;
+// om_path: 0 no offset/weight gradients, 1 LDS-window kernel, 2 general kernel.
+struct BwdPlan {
+    int x_path, cc, tile_sh, margin, x_lds;
+    int om_path;
+    OmPlan om;
+};
+void plan_backward(const Problem& p, const void* gout, bool want_x, bool want_om, BwdPlan* plan);
 hipError_t launch_backward(const Problem& p, const void* gout, float* gx, float* goff, float* gmask,
                            hipStream_t stream);
 

@@ -66,7 +66,8 @@ const Tune& tune()
         char buf[256];
         strncpy(buf, env, sizeof buf - 1);
         buf[sizeof buf - 1] = '\0';
-        for (char* tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+        char* save = nullptr;   // strtok_r: other threads may be parsing too
+        for (char* tok = strtok_r(buf, ",", &save); tok; tok = strtok_r(nullptr, ",", &save)) {
             char* eq = strchr(tok, '=');
             if (!eq) continue;
             *eq = '\0';
@@ -135,7 +136,7 @@ bool plan_window(const Problem& p, Plan* pl)
     // units of three or more vectors: one lane per vector (whole-unit lanes
     // need so many registers that a workgroup is capped at 512 threads)
     int lpu = (t.split == 1 && nv > 1) || (t.split < 0 && nv >= 3) ? nv : 1;
-    const int cus = kCus;
+    const int cus = p.cus;
 
     // group blocks to try, smallest first (all divisors of G unless tuned)
     int order[64], no = 0;

@@ -151,7 +151,10 @@ int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, v
  * to a multiple of 2^-F and summed exactly in
  * 64-bit integers (reproducible; F per (image, group) from the largest
  * |weight| * |grad_out| and the term count, so sums cannot overflow; the
- * binary32 path if either holds a non-finite value).  For K = 3 and larger
+ * binary32 path if either holds a non-finite value).  Each term's rounding
+ * error is then at most M * 2^-min(51, 62 - c), M = max|weight| * max|grad_out|
+ * over the (image, group) and 2^c >= 4 * P * Ho * Wo: at most M * 2^-40 for
+ * images with 4 * P * Ho * Wo <= 2^22 (256 x 256 outputs with K = 3).  For K = 3 and larger
  * images the same is done per 64 x 64-pixel tile (F per tile), for the units
  * whose grid centre lies within 16 pixels of the tile; terms from units
  * farther away are added with hardware atomic adds, so elements that receive
@@ -185,6 +188,10 @@ const char* dcnv4_version(void);
 /*
  * Launch plan the library would use for these arguments (for reporting and
  * tests).  Pure host computation, no HIP call.
+ * The planners size grids for the device's compute units (their count is
+ * read once per device at the first call on it); a plan query, which makes no
+ * HIP call, assumes an MI355X's 256.  The environment variable DCNV4_CUS
+ * (1..4096) overrides the count for both (tests; a partitioned device).
  */
 typedef struct dcnv4_plan {
     int kernel;           /* kernel family id, see dcnv4_kernel_name */
@@ -207,6 +214,31 @@ int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const 
                      int K, int stride, int pad, int dilation, float offset_scale,
                      int remove_center, int64_t offset_row, int64_t mask_row,
                      int dtype, dcnv4_plan* plan);
+
+/*
+ * The kernels dcnv4_backward would launch for these arguments (for reporting
+ * and tests).  Pure host computation, no HIP call.  need_x / need_offset_or_mask
+ * say which gradient pointers would be non-NULL.
+ */
+typedef struct dcnv4_backward_plan {
+    int x_path;        /* 0 no grad_x; 1 LDS fixed point over the whole bordered
+                          image; 2 LDS fixed point in square tiles (global atomic
+                          adds beyond the margin); 3 global atomic adds */
+    int x_channels;    /* paths 1, 2: channels per workgroup */
+    int x_tile;        /* path 2: tile side in pixels */
+    int x_margin;      /* path 2: pixels around a tile whose units it visits */
+    int x_lds_bytes;   /* paths 1, 2: LDS per workgroup, static included */
+    int om_path;       /* 0 none; 1 corners from LDS windows; 2 global gathers */
+    int om_tile_h, om_tile_w; /* om_path 1: output tile per workgroup */
+    int om_lds_bytes;  /* om_path 1: LDS per workgroup */
+} dcnv4_backward_plan;
+
+int dcnv4_query_backward_plan(const void* x, const void* offset, const void* mask, const void* grad_out,
+                              int need_x, int need_offset_or_mask,
+                              int N, int H, int W, int G, int Cg,
+                              int K, int stride, int pad, int dilation, float offset_scale,
+                              int remove_center, int64_t offset_row, int64_t mask_row,
+                              int dtype, dcnv4_backward_plan* plan);
 
 /* Name of a kernel family id from dcnv4_plan (static text). */
 const char* dcnv4_kernel_name(int kernel);

@@ -187,3 +187,77 @@ def test_backward_rejects_invalid_arguments(kw, status):
 def test_backward_empty_batch_and_no_gradients_are_noops():
     assert bcall(N=0, x=0, off=0, msk=0, gout=0, gx=0, goff=0, gm=0) == OK
     assert bcall(gx=0, goff=0, gm=0) == OK
+
+
+def bplan(need_x=1, need_om=1, **kw):
+    a = dict(x=X, off=OFF, msk=MSK, gout=GOUT, N=2, H=8, W=8, G=4, Cg=16, K=3, s=1, p=1, d=1, scale=1.0,
+             rc=0, orow=0, mrow=0, dtype=1)
+    a.update(kw)
+    pl = binding.BackwardPlan()
+    st = binding.lib().dcnv4_query_backward_plan(a["x"], a["off"], a["msk"], a["gout"], need_x, need_om,
+                                                 a["N"], a["H"], a["W"], a["G"], a["Cg"], a["K"], a["s"],
+                                                 a["p"], a["d"], a["scale"], a["rc"], a["orow"], a["mrow"],
+                                                 a["dtype"], ctypes.byref(pl))
+    return st, pl
+
+
+LDS_PER_CU = 160 * 1024
+
+
+@pytest.mark.parametrize("H,W,Cg,fill", [(30, 38, 16, "0"), (38, 62, 8, "0"), (62, 78, 4, "0"),
+                                          (30, 38, 16, None), (56, 56, 16, None), (14, 14, 16, None)])
+def test_backward_x_plan_fits_the_lds_with_the_static_part(H, W, Cg, fill, monkeypatch):
+    """The whole-image x-gradient kernel's accumulator plane plus its static
+    LDS must fit in the CU's 160 KiB.  The first three shapes' planes of 16,
+    8 and 4 channels are exactly 160 KiB, so they must take half as many."""
+    if fill is None:
+        monkeypatch.delenv("DCNV4_BWD_FILL", raising=False)
+    else:
+        monkeypatch.setenv("DCNV4_BWD_FILL", fill)
+    st, pl = bplan(N=64, H=H, W=W, G=4, Cg=Cg, dtype=0)
+    assert st == OK
+    assert pl.x_path in (1, 2)
+    assert 0 < pl.x_lds_bytes <= LDS_PER_CU
+    if pl.x_path == 1:
+        plane = (H + 2) * (W + 2) * 8
+        assert pl.x_lds_bytes >= plane * pl.x_channels
+        if plane * Cg == LDS_PER_CU:
+            assert pl.x_channels == Cg // 2
+
+
+def test_backward_plan_paths():
+    # K = 3, a stage-1 image: whole-image LDS kernels for both gradient kinds
+    st, pl = bplan(N=64, H=56, W=56, G=4, Cg=16, dtype=1)
+    assert st == OK and pl.as_dict()["x_path"] == "lds_whole" and pl.as_dict()["om_path"] == "lds_window"
+    # a 256 x 256 image: tiles
+    st, pl = bplan(N=2, H=256, W=256, G=8, Cg=16, dtype=2)
+    assert st == OK and pl.as_dict()["x_path"] == "lds_tiles" and pl.x_tile == 64
+    # K = 5: global atomics and gathers
+    st, pl = bplan(N=2, H=20, W=20, G=2, Cg=8, K=5, p=2, dtype=0)
+    assert st == OK and pl.as_dict()["x_path"] == "atomics" and pl.as_dict()["om_path"] == "global"
+    # nothing requested
+    st, pl = bplan(need_x=0, need_om=0)
+    assert st == OK and pl.x_path == 0 and pl.om_path == 0
+
+
+def test_planners_follow_the_compute_unit_count(monkeypatch):
+    """The GPU-filling rules size grids for the device's compute units
+    (DCNV4_CUS stands in for a smaller, partitioned device here): the
+    stage-1 shape at batch 8 has 32 (image, group) workgroups, too few for
+    256 CUs (more bands) but enough for 32."""
+    monkeypatch.delenv("DCNV4_CUS", raising=False)
+    st, pl = plan(dtype=1, Cg=16, N=8, H=56, W=56, G=4)
+    assert st == OK and pl.full_window == 0 and pl.grid == 256
+    monkeypatch.setenv("DCNV4_CUS", "32")
+    st, pl = plan(dtype=1, Cg=16, N=8, H=56, W=56, G=4)
+    assert st == OK and pl.full_window == 1 and pl.grid == 32
+    # the backward: with 256 CUs batch 4 takes x-gradient tiles, with 16 the whole image
+    monkeypatch.delenv("DCNV4_CUS")
+    st, pl = bplan(N=4, H=56, W=56, G=4, Cg=16, dtype=1)
+    assert st == OK and pl.as_dict()["x_path"] == "lds_tiles"
+    monkeypatch.setenv("DCNV4_CUS", "16")
+    st, pl = bplan(N=4, H=56, W=56, G=4, Cg=16, dtype=1)
+    assert st == OK and pl.as_dict()["x_path"] == "lds_whole"
+    monkeypatch.setenv("DCNV4_CUS", "not a number")
+    st, pl = plan(dtype=1, Cg=16, N=8, H=56, W=56, G=4)
+    assert st == OK and pl.grid == 256

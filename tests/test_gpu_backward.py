@@ -10,9 +10,10 @@ summation order.  The oracle returns those absolute sums and term counts:
   grad_x       n = number of scattered terms, c = 6
   grad_mask    n = 4*Cg products per point, c = 8
   grad_offset  n = 4*Cg products of differences per point, c = 10
-For K = 3 x's gradient is summed in 64-bit fixed point (each term rounded to
-a multiple of 2^-F, F fixed per (image, group) from max|m| * max|g| and the
-term-count bound, as the kernel states): each term adds at most 2^-(F+1).
+For K = 3 x's gradient is summed in 64-bit fixed point: the ABI states that
+each term's rounding is at most M * 2^-40, M = max|weight| * max|grad_out|
+over its (image, group), for images with 4 * P * Ho * Wo <= 2^22 (all shapes
+here), so the bound adds cnt_x * M * 2^-40 (fixed_point_allowance).
 """
 import numpy as np
 import pytest
@@ -58,35 +59,36 @@ def grad_out_for(wl, dtype, seed):
     return g
 
 
-def fixed_point_quantum(wl, m32, go32):
-    """Per-element bound of the fixed-point rounding of x's gradient: 2^-(F+1)
-    with F = min(62 - cbits, 51) - e (cbits < 11 takes 51), M = max|m| *
-    max|g| over the (image, group) in binary32, M < 2^e (as the LDS kernel
-    computes it); shaped like x."""
-    G, P, Cg = wl.G, wl.P, wl.Cg
+def fixed_point_allowance(wl, m32, go32):
+    """Per-element allowance for the fixed-point rounding of x's gradient
+    terms (K = 3), per the ABI: M * 2^-40 per term, M = max|m| * max|g| over
+    the (image, group), valid for 4 * P * Ho * Wo <= 2^22; shaped to
+    broadcast against x."""
     Ho, Wo = wl.out_hw()
-    cbits = int(np.ceil(np.log2(Ho * Wo * P * 4)))
+    assert 4 * wl.P * Ho * Wo <= 2 ** 22, "shape outside the stated fixed-point bound"
+    G, P, Cg = wl.G, wl.P, wl.Cg
     q = np.zeros((wl.N, 1, 1, G * Cg))
     for n in range(wl.N):
         for g in range(G):
-            mm = np.float32(np.abs(m32[n, ..., g * P:(g + 1) * P]).max())
-            mg = np.float32(np.abs(go32[n, ..., g * Cg:(g + 1) * Cg]).max())
-            M = np.float32(mm * mg)
-            F = 0
-            if M > 0:
-                _, e = np.frexp(M)
-                F = (51 if cbits < 11 else 62 - cbits) - int(e)
-            q[n, 0, 0, g * Cg:(g + 1) * Cg] = 2.0 ** (-(F + 1))
+            mm = float(np.abs(m32[n, ..., g * P:(g + 1) * P]).max())
+            mg = float(np.abs(go32[n, ..., g * Cg:(g + 1) * Cg]).max())
+            q[n, 0, 0, g * Cg:(g + 1) * Cg] = mm * mg * 2.0 ** -40
     return q
 
 
-def check(wl, dtype, seed=41, packed=False):
+def reference(wl, dtype, seed=41):
+    """Inputs and the oracle's gradients with their bound sums."""
     x, off, m = gen.make_inputs(wl, dtype)
     go = grad_out_for(wl, dtype, seed)
     kw = dict(K=wl.K, stride=wl.stride, pad=wl.pad, dil=wl.dil, offset_scale=wl.offset_scale,
               remove_center=wl.remove_center)
-    rx, roff, rm, rgo = f64(x, dtype), f64(off, dtype), f64(m, dtype), f64(go, dtype)
-    gx_ref, goff_ref, gm_ref, b = ref.backward_f64(rx, roff, rm, rgo, bounds=True, f32_positions=True, **kw)
+    gx_ref, goff_ref, gm_ref, b = ref.backward_f64(f64(x, dtype), f64(off, dtype), f64(m, dtype),
+                                                   f64(go, dtype), bounds=True, f32_positions=True, **kw)
+    return (x, off, m, go), (gx_ref, goff_ref, gm_ref, b)
+
+
+def check(wl, dtype, seed=41, packed=False, refs=None):
+    (x, off, m, go), (gx_ref, goff_ref, gm_ref, b) = refs or reference(wl, dtype, seed)
     G, P = wl.G, wl.P
     xd, god = gu.dev(x, dtype), gu.dev(go, dtype)
     if packed:
@@ -102,7 +104,7 @@ def check(wl, dtype, seed=41, packed=False):
     gx, goff, gm = (t.cpu().numpy().astype(np.float64) for t in (gx, goff, gm))
     tol_x = (b["cnt_x"] + 6) * U * b["abs_x"] + 1e-300
     if wl.K == 3:
-        tol_x = tol_x + b["cnt_x"] * fixed_point_quantum(wl, ref.to_f32(m, dtype), ref.to_f32(go, dtype))
+        tol_x = tol_x + b["cnt_x"] * fixed_point_allowance(wl, ref.to_f32(m, dtype), ref.to_f32(go, dtype))
     tol_m = (4 * wl.Cg + 8) * U * b["abs_mask"] + 1e-300
     tol_o = (4 * wl.Cg + 10) * U * b["abs_offset"] + 1e-300
     ex, em, eo = np.abs(gx - gx_ref), np.abs(gm - gm_ref), np.abs(goff - goff_ref)
@@ -123,6 +125,10 @@ for dtype in ("f32", "f16", "bf16"):
 for dtype, Cg in (("f16", 24), ("f16", 32), ("bf16", 24)):
     CASES.append((Workload("bwd", 2, 11, 13, 3, Cg, (dtype,), offset_dist=("normal", 2.0),
                            mask_dist=("normal", 0.7), seed=43), dtype))
+# an image whose plane of 16 channels' 64-bit accumulators is exactly the
+# CU's 160 KiB of LDS: the whole-image x-gradient kernel must take 8 channels
+# per workgroup to leave room for its static LDS
+CASES.append((Workload("bwd_lds_edge", 2, 30, 38, 2, 16, ("f32",), offset_dist=("normal", 2.0), seed=64), "f32"))
 for K, s, p, d, rc in ((5, 1, 2, 1, False), (3, 2, 1, 1, False), (3, 1, 2, 2, False), (3, 1, 1, 1, True),
                        (1, 1, 0, 1, False)):
     CASES.append((Workload("bwd_geom", 2, 12, 10, 2, 8, ("f32",), offset_dist=("normal", 1.5), K=K, stride=s,

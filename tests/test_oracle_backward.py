@@ -153,6 +153,106 @@ def test_bounds_dominate_the_gradients():
     assert np.array_equal(b["cnt_x"], np.round(b["cnt_x"])) and b["cnt_x"].max() >= 1
 
 
+def _nonnegative_case(rng, Hh=7, Ww=8, G=2, Cg=3, std=2.0, **geom):
+    """x, grad_out and weights >= 0 (weights on both sides of 1): every term
+    of grad_x and grad_mask is then >= 0."""
+    x, off, m, go, kw = case(rng, Hh=Hh, Ww=Ww, G=G, Cg=Cg, std=std, **geom)
+    return np.abs(x), off, 2.0 * np.abs(m), np.abs(go), kw
+
+
+def _positions(off, kw, Hh, Ww, scale):
+    """(pts, px, py): sampling positions of every (n, ho, wo, g, k) in float64,
+    p = base + scale * offset, with pts the (i, j) of point k."""
+    N, Ho, Wo, R = off.shape
+    K, s, p, d = kw["K"], kw["stride"], kw["pad"], kw["dil"]
+    pts = [(i, j) for i in range(K) for j in range(K) if not (kw["remove_center"] and i == K // 2 and j == K // 2)]
+    P = len(pts)
+    G = R // (2 * P)
+    o = off.reshape(N, Ho, Wo, G, 2, P)
+    ii = np.array([i for i, _ in pts], dtype=np.float64)
+    jj = np.array([j for _, j in pts], dtype=np.float64)
+    bx = (np.arange(Wo) * s - p)[None, None, :, None, None] + jj * d
+    by = (np.arange(Ho) * s - p)[None, :, None, None, None] + ii * d
+    return pts, bx + scale * o[..., 0, :], by + scale * o[..., 1, :]
+
+
+def _in_range(px, py, Hh, Ww):
+    return (px > -1) & (px < Ww) & (py > -1) & (py < Hh)
+
+
+GEOMS_B = [dict(), dict(K=3, stride=2, pad=0), dict(K=5, pad=2, dil=2), dict(rc=True)]
+
+
+@pytest.mark.parametrize("geom", GEOMS_B, ids=lambda g: ",".join(f"{k}={v}" for k, v in g.items()) or "default")
+def test_bound_sums_equal_the_gradients_when_every_term_is_nonnegative(geom):
+    """With x, grad_out and the weights >= 0 every term of grad_x and
+    grad_mask is >= 0, so their absolute-value sums are the gradients
+    themselves, exactly (same terms, same order).  A bound sum with a term
+    too many, a factor missing or a wrong corner differs."""
+    rng = np.random.default_rng(39)
+    x, off, m, go, kw = _nonnegative_case(rng, **geom)
+    gx, goff, gm, b = ref.backward_f64(x, off, m, go, bounds=True, **kw)
+    assert np.array_equal(b["abs_x"], gx) and gx.max() > 0
+    assert np.array_equal(b["abs_mask"], gm) and gm.max() > 0
+
+
+@pytest.mark.parametrize("geom", GEOMS_B, ids=lambda g: ",".join(f"{k}={v}" for k, v in g.items()) or "default")
+def test_term_counts_equal_a_brute_force_count(geom):
+    """cnt_x[q, c] = the number of (unit, point) pairs of c's group whose
+    sampling position is in range and within the triangle kernel's support
+    of pixel q (|py - qy| < 1 and |px - qx| < 1), counted by brute force over
+    every pixel.  Random offsets: no position is an integer."""
+    rng = np.random.default_rng(40)
+    Hh, Ww, G, Cg = 7, 8, 2, 3
+    x, off, m, go, kw = case(rng, Hh=Hh, Ww=Ww, G=G, Cg=Cg, std=2.0, **geom)
+    _, _, _, b = ref.backward_f64(x, off, m, go, bounds=True, **kw)
+    _, px, py = _positions(off, kw, Hh, Ww, 1.0)
+    want = np.zeros((x.shape[0], Hh, Ww, G))
+    qy = np.arange(Hh)[:, None]
+    qx = np.arange(Ww)[None, :]
+    for idx in np.ndindex(px.shape):
+        n, _, _, g, _ = idx
+        if not _in_range(px[idx], py[idx], Hh, Ww):
+            continue
+        want[n, :, :, g] += (np.abs(py[idx] - qy) < 1) & (np.abs(px[idx] - qx) < 1)
+    assert np.array_equal(b["cnt_x"], np.repeat(want, Cg, axis=-1))
+
+
+@pytest.mark.parametrize("geom", GEOMS_B, ids=lambda g: ",".join(f"{k}={v}" for k, v in g.items()) or "default")
+def test_offset_bound_sums_equal_a_brute_force_triangle_kernel_sum(geom):
+    """abs_offset of point k, plane x: |scale * m_k| times the sum over
+    channels c and every pixel q of |g_c| * tri(py - qy) * |dtri(px - qx)| *
+    |x[q, c]| (the absolute terms of d sample / d px in triangle-kernel form,
+    dtri = -1 on [0, 1) and +1 on [-1, 0)); plane y with the roles of the
+    axes exchanged.  Brute force over all pixels."""
+    rng = np.random.default_rng(41)
+    Hh, Ww, G, Cg = 6, 7, 2, 3
+    scale = 0.75
+    x, off, m, go, kw = case(rng, Hh=Hh, Ww=Ww, G=G, Cg=Cg, std=2.0, **geom)
+    _, _, _, b = ref.backward_f64(x, off, m, go, bounds=True, offset_scale=scale, **kw)
+    pts, px, py = _positions(off, kw, Hh, Ww, scale)
+    P = len(pts)
+    N, Ho, Wo, _ = off.shape
+    tri = lambda t: np.maximum(0.0, 1.0 - np.abs(t))  # noqa: E731
+    dtri_abs = lambda t: ((t >= -1) & (t < 1)).astype(np.float64)  # noqa: E731
+    want = np.zeros((N, Ho, Wo, G, 2, P))
+    qy = np.arange(Hh)[:, None]
+    qx = np.arange(Ww)[None, :]
+    mm = m.reshape(N, Ho, Wo, G, P)
+    for n, ho, wo, g, k in np.ndindex(N, Ho, Wo, G, P):
+        X, Y = px[n, ho, wo, g, k], py[n, ho, wo, g, k]
+        if not _in_range(X, Y, Hh, Ww):
+            continue
+        ax = np.abs(go[n, ho, wo, g * Cg:(g + 1) * Cg])           # |g_c|
+        f = np.abs(x[n, :, :, g * Cg:(g + 1) * Cg])               # |x[q, c]|
+        wx = (tri(Y - qy) * dtri_abs(X - qx))[..., None]
+        wy = (dtri_abs(Y - qy) * tri(X - qx))[..., None]
+        sm = abs(scale * mm[n, ho, wo, g, k])
+        want[n, ho, wo, g, 0, k] = sm * np.sum(wx * f * ax)
+        want[n, ho, wo, g, 1, k] = sm * np.sum(wy * f * ax)
+    np.testing.assert_allclose(b["abs_offset"], want.reshape(off.shape), rtol=1e-12, atol=0)
+
+
 def test_f32_positions_equal_exact_positions_for_dyadic_offsets():
     """Offsets that are multiples of 1/64 (and scale 0.5) give positions that
     binary32 represents exactly: both position modes agree exactly; with

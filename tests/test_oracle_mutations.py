@@ -43,6 +43,13 @@ MUTATIONS = {
     "bwd_scale_dropped": ("gox[s.P + k] = offset_scale * m * d_py;", "gox[s.P + k] = m * d_py;"),
     "bwd_grad_x_one_axis": ("grad_x[q + c] += m * ty * tx * go[c];", "grad_x[q + c] += m * ty * go[c];"),
     "bwd_grad_mask_abs": ("d_m += go[c] * ty * tx * f;", "d_m += fabs(go[c]) * ty * tx * f;"),
+    "bwd_bound_count_inflated": ("if (cnt_x) cnt_x[q + c] += 1.0;", "if (cnt_x) cnt_x[q + c] += 2.0;"),
+    "bwd_bound_x_weight_dropped": ("if (abs_x) abs_x[q + c] += fabs(m * ty * tx * go[c]);",
+                                   "if (abs_x) abs_x[q + c] += fabs(ty * tx * go[c]);"),
+    "bwd_bound_mask_one_axis": ("a_m += fabs(go[c] * ty * tx * f);", "a_m += fabs(go[c] * ty * f);"),
+    "bwd_bound_offset_weight_dropped": ("fabs(offset_scale * m) * a_px;", "fabs(offset_scale) * a_px;"),
+    "bwd_bound_offset_axis_factor_dropped": ("a_px += fabs(go[c] * ty * f);", "a_px += fabs(go[c] * f);"),
+    "bwd_bound_offset_y_doubled": ("fabs(offset_scale * m) * a_py;", "2.0 * fabs(offset_scale * m) * a_py;"),
     "sm_missing_normalisation": ("for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx) / sum;",
                                  "for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx);"),
     "sm_no_max_shift": ("for (int k = 0; k < P; ++k) sum += exp(m[k] - mx);\n            for (int k = 0; k < P; ++k) o[k] = exp(m[k] - mx) / sum;",
