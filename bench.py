@@ -17,7 +17,13 @@ stays full, so this is the kernel's duration plus the dispatch gap).
 Algorithmic bytes per (pixel, group) unit = (2*Cg + 3*P)*s: x read once, out
 written once, 2P offsets and P weights read once.  `roofline.traffic` = HBM
 bytes per launch measured by rocprofv3 counters on the same kernel source
-(profiles/<workload>_<dtype>_hbm_counters.json), else null.
+(profiles/<workload>_<dtype>_hbm_counters.json), else null; `l2_hit`
+= the L2 hit rate from the same counter runs (TCC_HIT / (TCC_HIT + TCC_MISS)).
+`configs` = every other measured configuration (the five workloads' I/O
+types), event-timed in the same run the same way, with each one's fraction
+of sampling points outside the image.  `cpu_baseline` = the CPU oracle on
+one thread and on all the cores the process may use (one thread per slice of
+images; the oracle itself stays single-threaded code).
 """
 import argparse
 import dataclasses
@@ -33,9 +39,10 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def load_traffic(workload, dtype, launches_bytes):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+def load_counters(workload, dtype):
+    """The committed rocprofv3 counter record of a workload (HBM bytes per
+    launch, L2 hits and misses), if it was taken on the current kernel
+    source; else None."""
     path = os.path.join(PROFILES, f"{workload}_{dtype}_hbm_counters.json")
     if not os.path.exists(path):
         return None
@@ -44,35 +51,63 @@ def load_traffic(workload, dtype, launches_bytes):
     from deformable_convolution_vision_dcnv4_amd.build import source_hash
     if rec.get("kernel_source_hash") != source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-def cpu_baseline(wl, dtype, x, off, m, budget_s):
-    """The CPU oracle (single-threaded C, as it stands) on the same inputs.
-
-    A bounded sample: whole passes over the first n images, n sized so that
-    one pass takes about budget_s; if the whole batch takes less, the batch is
-    repeated until about budget_s of CPU time has been spent."""
+def _oracle_rate(wl, dtype, x, off, m, budget_s, threads):
+    """Whole passes of the oracle over the first n images, n sized so that a
+    pass takes about budget_s (repeated while under budget_s), the images
+    split into `threads` contiguous slices run on as many threads (ctypes
+    releases the GIL for the C call).  Returns (bytes/s, samples/s, n, reps, s)."""
+    import concurrent.futures
     from oracle import ref
     kw = dict(K=wl.K, stride=wl.stride, pad=wl.pad, dil=wl.dil, offset_scale=wl.offset_scale,
               remove_center=wl.remove_center)
     t0 = time.perf_counter()
     ref.forward_f32(x[:1], off[:1], m[:1], dtype=dtype, **kw)
     per_img = max(time.perf_counter() - t0, 1e-6)
-    n = int(max(1, min(wl.N, budget_s / per_img)))
+    n = int(max(threads, min(wl.N, budget_s * threads / per_img)))
+    n = min(n, wl.N)
+    bounds = [(i * n // threads, (i + 1) * n // threads) for i in range(threads)]
+    bounds = [b for b in bounds if b[1] > b[0]]
+
+    def part(b):
+        ref.forward_f32(x[b[0]:b[1]], off[b[0]:b[1]], m[b[0]:b[1]], dtype=dtype, **kw)
+
     reps = 0
-    t0 = time.perf_counter()
-    while True:
-        ref.forward_f32(x[:n], off[:n], m[:n], dtype=dtype, **kw)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or dt + dt / reps > 3 * budget_s:
-            break
-    bytes_ = wl.algorithmic_bytes(dtype) * n / wl.N * reps
-    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} pass(es) over {n} of the workload's {wl.N} images (same inputs), "
-                      f"binary32-sequence oracle (plain C, one thread), {dt:.1f} s",
-            "gsamples_per_s": round(wl.samples() * n / wl.N * reps / dt / 1e9, 6)}
+    with concurrent.futures.ThreadPoolExecutor(len(bounds)) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(part, bounds))
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or dt + dt / reps > 3 * budget_s:
+                break
+    frac = n / wl.N * reps
+    return wl.algorithmic_bytes(dtype) * frac / dt, wl.samples() * frac / dt, n, reps, dt, len(bounds)
+
+
+def cpu_baseline(wl, dtype, x, off, m, budget_s):
+    """The CPU oracle (plain C, as it stands) on the same inputs: one thread,
+    then one thread per slice of images on every core the process may use
+    (at most 16, the host share of one GPU)."""
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    b1, s1, n1, r1, t1, _ = _oracle_rate(wl, dtype, x, off, m, budget_s, 1)
+    bc, sc, nc, rc, tc, used = _oracle_rate(wl, dtype, x, off, m, budget_s, cores)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(bc / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"{rc} pass(es) over {nc} of the workload's {wl.N} images (same inputs) split over {used} "
+                      f"threads, binary32-sequence oracle (plain C, single-threaded code), {tc:.1f} s; "
+                      f"one thread: {r1} pass(es) over {n1} images, {t1:.1f} s",
+            "gsamples_per_s": round(sc / 1e9, 6),
+            "single_thread": {"value": round(b1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "gsamples_per_s": round(s1 / 1e9, 6)},
+            "cpu_model": cpu_model}
 
 
 def main():
@@ -90,6 +125,8 @@ def main():
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotating input copies")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="time the named workload only")
+    ap.add_argument("--config-steps", type=int, default=50, help="timed launches per other configuration")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -103,7 +140,7 @@ def main():
 
     from deformable_convolution_vision_dcnv4_amd import binding
     from deformable_convolution_vision_dcnv4_amd import inputs as gen
-    from deformable_convolution_vision_dcnv4_amd.workloads import WORKLOADS
+    from deformable_convolution_vision_dcnv4_amd.workloads import CONFIGS, WORKLOADS, oob_fractions
 
     def log(*a):
         if not args.quiet:
@@ -116,116 +153,152 @@ def main():
         wl = dataclasses.replace(wl, name=f"{wl.name}_n{args.batch}", N=args.batch)
     dtype = args.dtype or wl.dtypes[-1]
     assert dtype in ("f32", "f16", "bf16")
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
-    dcode = {"f32": binding.F32, "f16": binding.F16, "bf16": binding.BF16}[dtype]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     binding.lib()
 
-    log(f"workload {wl.describe(dtype)}; generating inputs (seed {wl.seed})")
-    x, off, m = gen.make_inputs(wl, dtype)
+    def measure(wl, dtype, op, steps, warmup, rotate_gib, per_launch=True):
+        """Time `steps` back-to-back launches of `op` on wl's synthetic inputs
+        (resident in HBM, rotating over >= rotate_gib GiB of copies)."""
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+        dcode = {"f32": binding.F32, "f16": binding.F16, "bf16": binding.BF16}[dtype]
+        log(f"workload {wl.describe(dtype)}; generating inputs (seed {wl.seed})")
+        x, off, m = gen.make_inputs(wl, dtype)
 
-    def to_dev(a):
-        if dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
+        def to_dev(a):
+            if dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
 
-    Ho, Wo = wl.out_hw()
-    set_bytes = (x.nbytes + off.nbytes + m.nbytes + wl.N * Ho * Wo * wl.C * x.itemsize)
-    copies = int(min(64, max(2, -(-args.rotate_bytes * (1 << 30) // set_bytes))))
-    xs0, os0, ms0 = to_dev(x), to_dev(off), to_dev(m)
-    sets = []
-    for i in range(copies):
-        xi, oi, mi = (xs0, os0, ms0) if i == 0 else (xs0.clone(), os0.clone(), ms0.clone())
-        outi = torch.empty((wl.N, Ho, Wo, wl.C), dtype=tdt, device=dev)
-        sets.append((xi, oi, mi, outi))
-    torch.cuda.synchronize()
-    log(f"{copies} rotating input copies, {copies * set_bytes / 2**30:.2f} GiB")
-
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-    L = binding.lib()
-    argv = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr(), wl.N, wl.H, wl.W,
-             wl.G, wl.Cg, wl.K, wl.stride, wl.pad, wl.dil, wl.offset_scale, dcode, sptr) for s in sets]
-    fwd = L.dcnv4_forward
-    if args.op == "backward":
-        # grad_out: a copy of the output-shaped buffer filled with the forward's result;
-        # gradients in binary32, one set shared by all steps (each step overwrites them)
-        Pn = wl.P
-        gx = torch.empty((wl.N, wl.H, wl.W, wl.C), dtype=torch.float32, device=dev)
-        goff = torch.empty((wl.N, Ho, Wo, wl.G * 2 * Pn), dtype=torch.float32, device=dev)
-        gm = torch.empty((wl.N, Ho, Wo, wl.G * Pn), dtype=torch.float32, device=dev)
-        for a in argv:
-            assert fwd(*a) == 0
+        Ho, Wo = wl.out_hw()
+        set_bytes = (x.nbytes + off.nbytes + m.nbytes + wl.N * Ho * Wo * wl.C * x.itemsize)
+        copies = int(min(64, max(2, -(-rotate_gib * (1 << 30) // set_bytes))))
+        xs0, os0, ms0 = to_dev(x), to_dev(off), to_dev(m)
+        sets = []
+        for i in range(copies):
+            xi, oi, mi = (xs0, os0, ms0) if i == 0 else (xs0.clone(), os0.clone(), ms0.clone())
+            outi = torch.empty((wl.N, Ho, Wo, wl.C), dtype=tdt, device=dev)
+            sets.append((xi, oi, mi, outi))
         torch.cuda.synchronize()
-        bargv = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr(), gx.data_ptr(),
-                  goff.data_ptr(), gm.data_ptr(), wl.N, wl.H, wl.W, wl.G, wl.Cg, wl.K, wl.stride, wl.pad,
-                  wl.dil, wl.offset_scale, int(wl.remove_center), 0, 0, dcode, sptr) for s in sets]
-        bwd = L.dcnv4_backward
+        log(f"{copies} rotating input copies, {copies * set_bytes / 2**30:.2f} GiB")
 
-    if args.op == "softmax":
-        sm = L.dcnv4_forward_softmax
-        smargv = [a[:14] + (int(wl.remove_center), 0, 0) + a[14:] for a in argv]
+        stream = torch.cuda.current_stream()
+        sptr = stream.cuda_stream
+        L = binding.lib()
+        argv = [(st[0].data_ptr(), st[1].data_ptr(), st[2].data_ptr(), st[3].data_ptr(), wl.N, wl.H, wl.W,
+                 wl.G, wl.Cg, wl.K, wl.stride, wl.pad, wl.dil, wl.offset_scale, dcode, sptr) for st in sets]
+        fwd = L.dcnv4_forward
+        if op == "backward":
+            # grad_out: a copy of the output-shaped buffer filled with the forward's result;
+            # gradients in binary32, one set shared by all steps (each step overwrites them)
+            Pn = wl.P
+            gx = torch.empty((wl.N, wl.H, wl.W, wl.C), dtype=torch.float32, device=dev)
+            goff = torch.empty((wl.N, Ho, Wo, wl.G * 2 * Pn), dtype=torch.float32, device=dev)
+            gm = torch.empty((wl.N, Ho, Wo, wl.G * Pn), dtype=torch.float32, device=dev)
+            for a in argv:
+                assert fwd(*a) == 0
+            torch.cuda.synchronize()
+            bargv = [(st[0].data_ptr(), st[1].data_ptr(), st[2].data_ptr(), st[3].data_ptr(), gx.data_ptr(),
+                      goff.data_ptr(), gm.data_ptr(), wl.N, wl.H, wl.W, wl.G, wl.Cg, wl.K, wl.stride, wl.pad,
+                      wl.dil, wl.offset_scale, int(wl.remove_center), 0, 0, dcode, sptr) for st in sets]
+            bwd = L.dcnv4_backward
+        if op == "softmax":
+            sm = L.dcnv4_forward_softmax
+            smargv = [a[:14] + (int(wl.remove_center), 0, 0) + a[14:] for a in argv]
 
-    def step(i):
-        if args.op == "backward":
-            st = bwd(*bargv[i % copies])
-        elif args.op == "softmax":
-            st = sm(*smargv[i % copies])
-        else:
-            st = fwd(*argv[i % copies])
-        if st != 0:
-            raise RuntimeError(f"dcnv4 {args.op} failed: {binding.status_string(st)}: {binding.last_error()}")
+        def step(i):
+            if op == "backward":
+                st = bwd(*bargv[i % copies])
+            elif op == "softmax":
+                st = sm(*smargv[i % copies])
+            else:
+                st = fwd(*argv[i % copies])
+            if st != 0:
+                raise RuntimeError(f"dcnv4 {op} failed: {binding.status_string(st)}: {binding.last_error()}")
 
-    plan = binding.query_plan(sets[0][0], sets[0][1], sets[0][2], sets[0][3], kernel_size=wl.K,
-                              stride=wl.stride, pad=wl.pad, dilation=wl.dil, offset_scale=wl.offset_scale)
-    log(f"plan {plan}")
+        plan = binding.query_plan(sets[0][0], sets[0][1], sets[0][2], sets[0][3], kernel_size=wl.K,
+                                  stride=wl.stride, pad=wl.pad, dilation=wl.dil, offset_scale=wl.offset_scale)
+        log(f"plan {plan}")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        log(f"warmup {warmup} done")
 
-    # timed region: K back-to-back launches between two events on the launch stream
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    region_ms = ev0.elapsed_time(ev1)
-    kern_ms = region_ms / args.steps
-    log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, events {region_ms:.3f} ms, "
-        f"{kern_ms * 1e3:.2f} us per launch")
+        # timed region: K back-to-back launches between two events on the launch stream
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        region_ms = ev0.elapsed_time(ev1)
+        kern_ms = region_ms / steps
+        log(f"timed {steps} steps: wall {wall * 1e3:.3f} ms, events {region_ms:.3f} ms, "
+            f"{kern_ms * 1e3:.2f} us per launch")
+        r = {"wall_s": wall, "kern_ms": kern_ms, "copies": copies, "plan": plan, "inputs": (x, off, m)}
+        if per_launch:
+            # secondary: one event pair per launch (adds the events' own cost; for a
+            # short kernel it also shows host-side launch latency)
+            starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            for i in range(steps):
+                starts[i].record(stream)
+                step(i)
+                ends[i].record(stream)
+            torch.cuda.synchronize()
+            durs = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms
+            log(f"per-launch event pairs: median {np.median(durs) * 1e3:.2f} us, "
+                f"p10 {np.percentile(durs, 10) * 1e3:.2f} us, p90 {np.percentile(durs, 90) * 1e3:.2f} us")
+            r["median_ms"] = float(np.median(durs))
+        del sets
+        torch.cuda.empty_cache()
+        return r
 
-    # secondary: one event pair per launch (adds the events' own cost; for a
-    # short kernel it also shows host-side launch latency)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
-    log(f"per-launch event pairs: median {np.median(durs) * 1e3:.2f} us, "
-        f"p10 {np.percentile(durs, 10) * 1e3:.2f} us, p90 {np.percentile(durs, 90) * 1e3:.2f} us")
-
+    r = measure(wl, dtype, args.op, args.steps, args.warmup, args.rotate_bytes)
+    x, off, m = r["inputs"]
     alg_bytes = wl.backward_bytes(dtype) if args.op == "backward" else wl.algorithmic_bytes(dtype)
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = r["wall_s"] * 1e3 / args.steps
+    kern_ms = r["kern_ms"]
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name if args.op == "forward" else f"{wl.name}_{args.op}", dtype, alg_bytes)
+    counters = load_counters(wl.name if args.op == "forward" else f"{wl.name}_{args.op}", dtype)
+
+    # the other configurations, timed the same way (launch-to-launch events)
+    configs = []
+    if args.op == "forward" and not args.no_configs and args.batch is None:
+        for name, cdt in CONFIGS:
+            if (name, cdt) == (wl.name, dtype):
+                continue
+            cwl = WORKLOADS[name]
+            cr = measure(cwl, cdt, "forward", args.config_steps, max(5, args.warmup // 4), args.rotate_bytes,
+                         per_launch=False)
+            cbytes = cwl.algorithmic_bytes(cdt)
+            ccnt = load_counters(name, cdt)
+            oob, corner = oob_fractions(cwl, gen.as_f64(cr["inputs"][1], cdt))
+            configs.append({
+                "workload": cwl.describe(cdt), "dtype": cdt, "kernel_us_mean": round(cr["kern_ms"] * 1e3, 3),
+                "gbs": round(cbytes / (cr["kern_ms"] * 1e-3) / 1e9, 2),
+                "hbm_fraction": round(cbytes / (cr["kern_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "gsamples_per_s": round(cwl.samples() / (cr["kern_ms"] * 1e-3) / 1e9, 3),
+                "algorithmic_bytes": cbytes, "steps": args.config_steps,
+                "plan": {k: cr["plan"][k] for k in ("kernel", "lanes_per_unit", "block", "grid", "tile_h", "tile_w",
+                                                      "full_window")},
+                "points_outside": round(oob, 4), "points_with_a_corner_outside": round(corner, 4),
+                "l2_hit": ccnt.get("l2_hit") if ccnt else None,
+                "hbm_traffic": ccnt.get("hbm_bytes_per_launch") if ccnt else None,
+            })
 
     cpu = None
     if not args.no_cpu_baseline and args.op == "forward":
         log("timing the CPU oracle baseline")
         cpu = cpu_baseline(wl, dtype, x, off, m, args.cpu_budget)
 
+    oob, corner = oob_fractions(wl, gen.as_f64(off, dtype))
     rec = {
         "metric": {"forward": "DCNv4 fwd GB/s + Gsamples/s per MI355X; % of HBM roofline",
                    "backward": "DCNv4 bwd GB/s + Gsamples/s per MI355X; % of HBM roofline",
@@ -250,21 +323,25 @@ def main():
                        "seed": wl.seed},
             "algorithmic_bytes_per_step": alg_bytes,
             "samples_per_step": wl.samples(),
-            "rotating_copies": copies,
-            "plan": plan,
+            "rotating_copies": r["copies"],
+            "plan": r["plan"],
+            "points_outside": round(oob, 4),
+            "points_with_a_corner_outside": round(corner, 4),
         },
         "gsamples_per_s": round(wl.samples() / (ms_per_step * 1e-3) / 1e9, 3),
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "kernel_us_mean": round(kern_ms * 1e3, 3),
-        "per_launch_event_us_median": round(float(np.median(durs)) * 1e3, 3),
+        "per_launch_event_us_median": round(r["median_ms"] * 1e3, 3),
+        "l2_hit": counters.get("l2_hit") if counters else None,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": counters.get("hbm_bytes_per_launch") if counters else None,
         },
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -8,7 +8,12 @@
           the per-kernel table (calls, mean/min/max duration) is kept.
 --fetch:  a `rocprofv3 --pmc FETCH_SIZE --output-format csv` directory;
 --write:  a `rocprofv3 --pmc WRITE_SIZE --output-format csv` directory.
-          Both counters are in KiB per dispatch.  Each is scaled by the
+          Both counters are in KiB per dispatch.  Other counters found in the
+          same runs are summarised too: TCC_HIT_sum / TCC_MISS_sum (L2 hit
+          rate), SQ_INSTS_VALU, SQ_INSTS_VALU_FMA_F32, SQ_INSTS_LDS (wave
+          instructions, reported per (pixel, group) unit as lane operations:
+          x 64 / units), SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of
+          LDS-busy cycles lost to bank conflicts).  Each is scaled by the
           factor that makes it read the known size of the plain device-to-
           device copies bench.py makes of its inputs (the rotating copies:
           each copies x, offset and mask once, so it reads and writes exactly
@@ -71,6 +76,45 @@ def scaled_counter(d, counter, copy_bytes_each):
     known = sum(copy_bytes_each[i % 3] for i in range(len(copies)))
     factor = known / (sum(copies) * 1024.0)
     return statistics.mean(ops), factor, len(ops), len(copies)
+
+
+def op_mean(dirs, counter):
+    """Mean over the operator's dispatches of `counter` in the first of
+    `dirs` that holds it; None if none does."""
+    for d in dirs:
+        if not d:
+            continue
+        try:
+            rows = counter_rows(d, counter)
+        except SystemExit:
+            continue
+        ops = [v for n, v in rows if is_op(n)]
+        if ops:
+            return statistics.mean(ops)
+    return None
+
+
+def extra_counters(dirs, units):
+    """L2 hit rate and per-unit instruction counts from whatever of these
+    counters the runs collected."""
+    out = {}
+    hit, miss = op_mean(dirs, "TCC_HIT_sum"), op_mean(dirs, "TCC_MISS_sum")
+    if hit is not None and miss is not None and hit + miss > 0:
+        out["l2_hit"] = round(hit / (hit + miss), 4)
+        out["l2_hits"] = round(hit)
+        out["l2_misses"] = round(miss)
+    for name, key in (("SQ_INSTS_VALU", "valu_lane_ops_per_unit"), ("SQ_INSTS_VALU_FMA_F32", "fma_f32_lane_ops_per_unit"),
+                      ("SQ_INSTS_LDS", "lds_lane_ops_per_unit")):
+        v = op_mean(dirs, name)
+        if v is not None:
+            out[key] = round(v * 64 / units, 1)
+            out[name] = round(v)
+    bc, act = op_mean(dirs, "SQ_LDS_BANK_CONFLICT"), op_mean(dirs, "SQ_LDS_IDX_ACTIVE")
+    if bc is not None and act:
+        out["lds_bank_conflict_share"] = round(bc / act, 3)
+        out["SQ_LDS_BANK_CONFLICT"] = round(bc)
+        out["SQ_LDS_IDX_ACTIVE"] = round(act)
+    return out
 
 
 def main(argv=None):
@@ -143,6 +187,8 @@ def main(argv=None):
                "hbm_bytes_per_launch": round(fetch_b + write_b),
                "algorithmic_read_bytes": x_b + off_b + m_b, "algorithmic_write_bytes": x_b,
                "algorithmic_bytes_per_launch": alg}
+        extra = extra_counters([a.fetch, a.write], wl.units()) if a.op == "forward" else {}
+        rec.update(extra)
         with open(a.out + "_hbm_counters.json", "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
@@ -154,6 +200,16 @@ def main(argv=None):
             f"factor {w_fac:.4f} -> {write_b / 1e6:.2f} MB written (algorithmic {x_b / 1e6:.2f} MB)",
             f"HBM traffic per launch: {(fetch_b + write_b) / 1e6:.2f} MB = "
             f"{(fetch_b + write_b) / alg:.3f} x algorithmic"]
+        if "l2_hit" in extra:
+            lines.append(f"L2 (TCC) hit rate: {extra['l2_hit']:.3f} ({extra['l2_hits']} hits, "
+                         f"{extra['l2_misses']} misses per dispatch)")
+        if "valu_lane_ops_per_unit" in extra:
+            lines.append(f"VALU: {extra['valu_lane_ops_per_unit']:.0f} lane operations per (pixel, group) unit "
+                         f"(SQ_INSTS_VALU {extra['SQ_INSTS_VALU']} wave instructions per dispatch); "
+                         f"FP32 FMA {extra.get('fma_f32_lane_ops_per_unit', float('nan')):.0f} per unit")
+        if "lds_lane_ops_per_unit" in extra:
+            lines.append(f"LDS: {extra['lds_lane_ops_per_unit']:.0f} lane operations per unit; bank conflicts "
+                         f"{extra.get('lds_bank_conflict_share', float('nan')):.3f} of LDS-busy cycles")
         with open(a.out + "_hbm_counters.txt", "w") as fh:
             fh.write("\n".join(lines) + "\n")
     return 0

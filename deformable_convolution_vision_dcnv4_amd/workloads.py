@@ -97,3 +97,32 @@ WORKLOADS = {
                           mask_dist=("normal", 1.0 / math.sqrt(8.0)),
                           note="diffusion U-Net latent shape, Cg=40"),
 }
+
+
+# Every configuration the operator is measured and parity-tested on:
+# (workload, I/O type).  fiit_stage1 in f16 is the headline.
+CONFIGS = (("tiny", "f32"), ("fiit_stage1", "f32"), ("fiit_stage1", "f16"), ("fiit_stage3", "f16"),
+           ("hires", "bf16"), ("sd_latent", "bf16"))
+
+
+def oob_fractions(wl, offset_f64):
+    """Reporting statistic of a workload's offsets (float64 values of the
+    inputs, [N, Ho, Wo, G*2*P]): the fraction of sampling points whose
+    position lies outside (-1, H) x (-1, W) (they contribute nothing), and
+    the fraction with at least one of their four corners outside the image."""
+    import numpy as np
+    Ho, Wo = wl.out_hw()
+    P, G = wl.P, wl.G
+    pts = [(i, j) for i in range(wl.K) for j in range(wl.K)
+           if not (wl.remove_center and i == wl.K // 2 and j == wl.K // 2)]
+    ii = np.array([i for i, _ in pts], dtype=np.float64)
+    jj = np.array([j for _, j in pts], dtype=np.float64)
+    o = offset_f64.reshape(wl.N, Ho, Wo, G, 2, P)
+    bx = (np.arange(Wo) * wl.stride - wl.pad)[None, None, :, None, None] + jj * wl.dil
+    by = (np.arange(Ho) * wl.stride - wl.pad)[None, :, None, None, None] + ii * wl.dil
+    px = bx + wl.offset_scale * o[..., 0, :]
+    py = by + wl.offset_scale * o[..., 1, :]
+    outside = ~((px > -1) & (px < wl.W) & (py > -1) & (py < wl.H))
+    fx, fy = np.floor(px), np.floor(py)
+    corner_out = (fx < 0) | (fx + 1 > wl.W - 1) | (fy < 0) | (fy + 1 > wl.H - 1)
+    return float(outside.mean()), float((corner_out | outside).mean())

@@ -72,6 +72,48 @@ def test_summary_scales_counters_by_copy_calibration(tmp_path):
     assert f"{gbs:.1f} GB/s" in txt
 
 
+def test_summary_reports_l2_hit_rate_and_per_unit_counts(tmp_path):
+    """Counters collected beside FETCH_SIZE / WRITE_SIZE in the same runs:
+    L2 hit rate = hits / (hits + misses); wave instructions x 64 / units;
+    bank-conflict cycles / LDS-busy cycles."""
+    import csv as _csv
+    wl = WORKLOADS["fiit_stage1"]
+    units = wl.units()
+
+    def multi(path, entries):
+        hdr = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+               "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+               "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w", newline="") as fh:
+            w = _csv.writer(fh, quoting=_csv.QUOTE_NONNUMERIC)
+            w.writerow(hdr)
+            d = 0
+            for name, counter, v in entries:
+                d += 1
+                w.writerow([d, d, "Agent 1", 1, 1, 1, 1, 1, name, 1024, 0, 0, 128, 0, 64, counter, v, 0, 1])
+
+    copy = "__amd_rocclr_copyBuffer"
+    f_entries = [(copy, "FETCH_SIZE", 1.0)] * 3 + [(OP, "FETCH_SIZE", 2.0)]
+    f_entries += [(OP, "SQ_INSTS_VALU", units * 1000 / 64), (OP, "SQ_INSTS_LDS", units * 80 / 64),
+                  (OP, "SQ_LDS_BANK_CONFLICT", 30.0), (OP, "SQ_LDS_IDX_ACTIVE", 120.0),
+                  (copy, "SQ_INSTS_VALU", 5.0)]
+    w_entries = [(copy, "WRITE_SIZE", 1.0)] * 3 + [(OP, "WRITE_SIZE", 2.0), (OP, "TCC_HIT_sum", 300.0),
+                                                   (OP, "TCC_MISS_sum", 100.0), (copy, "TCC_HIT_sum", 7.0)]
+    multi(str(tmp_path / "f" / "pmc_counter_collection.csv"), f_entries)
+    multi(str(tmp_path / "w" / "pmc_counter_collection.csv"), w_entries)
+    out = str(tmp_path / "o" / "x")
+    os.makedirs(os.path.dirname(out))
+    assert rocprof_summary.main(["--workload", "fiit_stage1", "--dtype", "f16", "--fetch", str(tmp_path / "f"),
+                                 "--write", str(tmp_path / "w"), "--command", "C", "--out", out]) == 0
+    rec = json.load(open(out + "_hbm_counters.json"))
+    assert rec["l2_hit"] == 0.75
+    assert rec["valu_lane_ops_per_unit"] == 1000.0 and rec["lds_lane_ops_per_unit"] == 80.0
+    assert rec["lds_bank_conflict_share"] == 0.25
+    txt = open(out + "_hbm_counters.txt").read()
+    assert "L2 (TCC) hit rate: 0.750" in txt and "1000 lane operations per (pixel, group) unit" in txt
+
+
 def test_source_hash_is_stable_and_short():
     h = build.source_hash()
     assert h == build.source_hash() and len(h) == 16
