@@ -21,7 +21,27 @@ _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 # Every symbol include/dcnv4.h declares.
 EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_forward_softmax", "dcnv4_backward", "dcnv4_output_dim",
            "dcnv4_status_string", "dcnv4_last_error", "dcnv4_version", "dcnv4_query_plan",
-           "dcnv4_query_backward_plan", "dcnv4_kernel_name")
+           "dcnv4_query_backward_plan", "dcnv4_kernel_name", "dcnv4_module_workspace_layout",
+           "dcnv4_module_forward")
+
+NORM_NONE, NORM_GROUP, NORM_LAYER = 0, 1, 2
+
+
+class ModuleConfig(ctypes.Structure):
+    _fields_ = [("Cin", ctypes.c_int), ("G", ctypes.c_int), ("Cg", ctypes.c_int), ("Cout", ctypes.c_int),
+                ("norm", ctypes.c_int), ("norm_groups", ctypes.c_int), ("eps", ctypes.c_float),
+                ("remove_center", ctypes.c_int), ("center_scale", ctypes.c_int), ("out_proj", ctypes.c_int),
+                ("offset_scale", ctypes.c_float)]
+
+
+class ModuleWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in ("w_in", "b_in", "gamma", "beta", "w_dw", "b_dw", "w_pred",
+                                                     "b_pred", "w_out", "b_out")]
+
+
+class ModuleLayout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in ("xp", "xn", "d", "rows", "y", "gated", "stats", "rows_stride",
+                                                    "total")]
 
 
 class Plan(ctypes.Structure):
@@ -90,6 +110,12 @@ def lib():
         L.dcnv4_query_backward_plan.argtypes = [vp] * 4 + [i32] * 11 + [f32, i32, i64, i64, i32,
                                                                           ctypes.POINTER(BackwardPlan)]
         L.dcnv4_query_backward_plan.restype = i32
+        L.dcnv4_module_workspace_layout.argtypes = [i32, i32, i32, ctypes.POINTER(ModuleConfig), i32,
+                                                     ctypes.POINTER(ModuleLayout)]
+        L.dcnv4_module_workspace_layout.restype = i32
+        L.dcnv4_module_forward.argtypes = [vp, ctypes.POINTER(ModuleWeights), vp, i32, i32, i32,
+                                           ctypes.POINTER(ModuleConfig), vp, ctypes.c_size_t, i32, vp]
+        L.dcnv4_module_forward.restype = i32
         L.dcnv4_kernel_name.argtypes = [i32]
         L.dcnv4_kernel_name.restype = ctypes.c_char_p
         _lib = L
@@ -284,3 +310,56 @@ def query_backward_plan(x, offset, mask, grad_out, *, kernel_size=3, stride=1, p
                                            1 if remove_center else 0, orow, mrow, _DTYPE_CODE[x.dtype],
                                            ctypes.byref(pl)))
     return pl.as_dict()
+
+
+def module_config(*, Cin, G, Cg, Cout=None, norm=NORM_GROUP, norm_groups=32, eps=1e-5, remove_center=False,
+                  center_scale=False, out_proj=False, offset_scale=1.0):
+    """The module's options as the C struct (Cout defaults to G*Cg)."""
+    return ModuleConfig(int(Cin), int(G), int(Cg), int(Cout if Cout is not None else G * Cg), int(norm),
+                        int(norm_groups), float(eps), int(bool(remove_center)), int(bool(center_scale)),
+                        int(bool(out_proj)), float(offset_scale))
+
+
+def module_layout(N, H, W, cfg, dtype):
+    """Workspace layout (dict of byte offsets, -1 for unused regions)."""
+    lay = ModuleLayout()
+    _check(lib().dcnv4_module_workspace_layout(int(N), int(H), int(W), ctypes.byref(cfg), _DTYPE_CODE[dtype],
+                                               ctypes.byref(lay)))
+    return {name: getattr(lay, name) for name, _ in lay._fields_}
+
+
+def module_forward(x, weights, cfg, *, out=None, workspace=None, stream=None):
+    """DCNv4 module forward (include/dcnv4_module.h) on x [N, H, W, Cin].
+
+    weights: dict of tensors on x's device -- w_in [C, Cin], w_pred [R, C],
+    w_out [Cout, C] in x's dtype; b_in, gamma, beta, w_dw [C, 3, 3], b_dw,
+    b_pred, b_out in float32 (gamma/beta, w_out/b_out only when used).
+    Returns (out [N, H, W, Cout], workspace, layout); the workspace (a uint8
+    tensor, allocated here unless given) holds the intermediates at the
+    layout's byte offsets."""
+    if x.dim() != 4 or not x.is_contiguous() or x.dtype not in _DTYPE_CODE:
+        raise ValueError("x must be a contiguous [N, H, W, Cin] tensor of float32, float16 or bfloat16")
+    N, H, W, Cin = x.shape
+    if Cin != cfg.Cin:
+        raise ValueError(f"x has {Cin} channels, the config {cfg.Cin}")
+    lay = module_layout(N, H, W, cfg, x.dtype)
+    if out is None:
+        out = torch.empty((N, H, W, cfg.Cout), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(lay["total"], 256), dtype=torch.uint8, device=x.device)
+    wts = ModuleWeights()
+    for name, _ in wts._fields_:
+        t = weights.get(name)
+        if t is not None:
+            if t.device != x.device or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor on {x.device}")
+            setattr(wts, name, t.data_ptr())
+    if stream is None:
+        with torch.cuda.device(x.device):
+            stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(x.device):
+        _check(lib().dcnv4_module_forward(x.data_ptr(), ctypes.byref(wts), out.data_ptr(), N, H, W,
+                                          ctypes.byref(cfg), workspace.data_ptr(), workspace.numel(),
+                                          _DTYPE_CODE[x.dtype], sptr))
+    return out, workspace, lay

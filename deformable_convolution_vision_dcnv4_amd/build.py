@@ -34,7 +34,7 @@ def source_hash():
     build, so that counter measurements can be matched to the code they
     were taken on."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(INCLUDE, "dcnv4.h")]
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
     for path in files:
         if not os.path.isfile(path) or path.endswith((".so", ".tmp")):
             continue

@@ -20,10 +20,11 @@
 #include "dcnv4_internal.h"
 
 namespace {
-
 thread_local char g_last_error[256] = "";
+}  // namespace
 
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+namespace dcnv4 {
+
 int fail(int status, const char* fmt, ...)
 {
     va_list ap;
@@ -32,6 +33,14 @@ int fail(int status, const char* fmt, ...)
     va_end(ap);
     return status;
 }
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+}  // namespace dcnv4
+
+namespace {
+
+using dcnv4::fail;
 
 int out_dim(int in, int K, int stride, int pad, int dil)
 {
@@ -48,17 +57,7 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-// Compute units the planners size their grids for: DCNV4_CUS (1..4096) when
-// set (tests of the planners; a partitioned device), else the device's count,
-// else (plan queries, which make no HIP call) an MI355X's 256.
-int planner_cus(int device_cus)
-{
-    if (const char* e = getenv("DCNV4_CUS")) {
-        const int v = atoi(e);
-        if (v >= 1 && v <= 4096) return v;
-    }
-    return device_cus > 0 ? device_cus : dcnv4::kDefaultCus;
-}
+using dcnv4::planner_cus;
 
 // Validate and fill a Problem.  Returns DCNV4_OK or an error status.  With
 // check_pointers false only the shapes and parameters are checked (the
@@ -136,6 +135,22 @@ int validate(dcnv4::Problem* p, const void* x, const void* offset, const void* m
     return DCNV4_OK;
 }
 
+}  // namespace
+
+namespace dcnv4 {
+
+// Compute units the planners size their grids for: DCNV4_CUS (1..4096) when
+// set (tests of the planners; a partitioned device), else the device's count,
+// else (plan queries, which make no HIP call) an MI355X's 256.
+int planner_cus(int device_cus)
+{
+    if (const char* e = getenv("DCNV4_CUS")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= 4096) return v;
+    }
+    return device_cus > 0 ? device_cus : kDefaultCus;
+}
+
 // Is the current device a gfx950?  Cached per device id, with its compute
 // unit count (multiProcessorCount), returned in *cus.
 int check_device(int* cus)
@@ -166,6 +181,12 @@ int check_device(int* cus)
     *cus = cu_count[dev];
     return DCNV4_OK;
 }
+
+}  // namespace dcnv4
+
+namespace {
+
+using dcnv4::check_device;
 
 int forward_impl(const void* x, const void* offset, const void* mask, void* out,
                  int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,

@@ -53,6 +53,14 @@ constexpr int kDefaultCus = 256;
 // accumulator plane plus this must fit in kLdsPerCu.
 constexpr int kBwdXStaticLds = 256;
 
+// The ABI layer's shared pieces (dcnv4_host.hip): record the calling
+// thread's last error (returns `status`), clear it, the compute units the
+// planners use, and the gfx950 check of the current device (its CU count).
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int planner_cus(int device_cus);
+int check_device(int* cus);
+
 // Pure host: pick the kernel and launch shape for a validated problem.
 void make_plan(const Problem& p, Plan* plan);
 

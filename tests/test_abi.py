@@ -1,6 +1,7 @@
 """The C ABI on the CPU: the library loads, exports every declared symbol, and
 rejects every invalid argument before touching HIP (no GPU needed)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,7 +10,7 @@ import pytest
 from deformable_convolution_vision_dcnv4_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dcnv4.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_DTYPE, ERR_ALIAS, ERR_TOO_LARGE, ERR_HIP, ERR_ALIGN = range(9)
 
@@ -18,7 +19,7 @@ X, OFF, MSK, OUT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dcnv4_[a-z_0-9]+)\s*\(", text)))
 
