@@ -22,7 +22,9 @@ _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 EXPORTS = ("dcnv4_forward", "dcnv4_forward_ex", "dcnv4_forward_softmax", "dcnv4_backward", "dcnv4_output_dim",
            "dcnv4_status_string", "dcnv4_last_error", "dcnv4_version", "dcnv4_query_plan",
            "dcnv4_query_backward_plan", "dcnv4_kernel_name", "dcnv4_module_workspace_layout",
-           "dcnv4_module_forward")
+           "dcnv4_module_forward", "dcnv4_module_forward_noalloc")
+
+MODULE_SCRATCH_BYTES = 64 << 20   # DCNV4_MODULE_SCRATCH_BYTES
 
 NORM_NONE, NORM_GROUP, NORM_LAYER = 0, 1, 2
 
@@ -116,6 +118,9 @@ def lib():
         L.dcnv4_module_forward.argtypes = [vp, ctypes.POINTER(ModuleWeights), vp, i32, i32, i32,
                                            ctypes.POINTER(ModuleConfig), vp, ctypes.c_size_t, i32, vp]
         L.dcnv4_module_forward.restype = i32
+        L.dcnv4_module_forward_noalloc.argtypes = [vp, ctypes.POINTER(ModuleWeights), vp, i32, i32, i32,
+                                                   ctypes.POINTER(ModuleConfig), i32, vp]
+        L.dcnv4_module_forward_noalloc.restype = i32
         L.dcnv4_kernel_name.argtypes = [i32]
         L.dcnv4_kernel_name.restype = ctypes.c_char_p
         _lib = L

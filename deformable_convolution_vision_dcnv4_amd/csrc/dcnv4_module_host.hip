@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "dcnv4.h"
@@ -122,13 +124,16 @@ int dcnv4_module_workspace_layout(int N, int H, int W, const dcnv4_module_config
     return DCNV4_OK;
 }
 
-int dcnv4_module_forward(const void* x_in, const dcnv4_module_weights* w, void* out,
-                         int N, int H, int W, const dcnv4_module_config* cfg,
-                         void* workspace, size_t workspace_bytes, int dtype, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Validate a call whose workspace is `workspace` (workspace_bytes) and launch it.
+int module_forward_impl(const void* x_in, const dcnv4_module_weights* w, void* out, int N, int H, int W,
+                        const dcnv4_module_config* cfg, void* workspace, size_t workspace_bytes, int dtype,
+                        void* stream, const ModuleLayout& L)
 {
-    ModuleLayout L;
-    int st = validate_config(N, H, W, cfg, dtype, &L);
-    if (st != DCNV4_OK) return st;
+    int st;
     if (N == 0) return DCNV4_OK;
     if (!w) return fail(DCNV4_ERR_NULL, "weights is null");
     const bool gn = cfg->norm != DCNV4_NORM_NONE;
@@ -178,6 +183,77 @@ int dcnv4_module_forward(const void* x_in, const dcnv4_module_weights* w, void* 
     const hipError_t e = dcnv4::launch_module(m, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DCNV4_ERR_HIP, "launch of the module failed: %s", hipGetErrorString(e));
     return DCNV4_OK;
+}
+
+
+// The no-allocation variant's workspace: one array per device, in the code
+// object's data (loaded with the library), never allocated or freed by a
+// call.  Host code uses only its device address from hipGetSymbolAddress:
+// the array's name stands for a host-side shadow, not device memory.
+static __device__ __align__(256) unsigned char scratch[DCNV4_MODULE_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr after a failure
+// (recorded as the call's error).
+void* scratch_address()
+{
+    static std::mutex mu;
+    static void* addr[64];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        fail(DCNV4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= 64) {
+        fail(DCNV4_ERR_HIP, "device id %d out of range", dev);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(DCNV4_ERR_HIP, "hipGetSymbolAddress of the module scratch array: %s", hipGetErrorString(e));
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int dcnv4_module_forward(const void* x_in, const dcnv4_module_weights* w, void* out,
+                         int N, int H, int W, const dcnv4_module_config* cfg,
+                         void* workspace, size_t workspace_bytes, int dtype, void* stream)
+{
+    ModuleLayout L;
+    const int st = validate_config(N, H, W, cfg, dtype, &L);
+    if (st != DCNV4_OK) return st;
+    return module_forward_impl(x_in, w, out, N, H, W, cfg, workspace, workspace_bytes, dtype, stream, L);
+}
+
+int dcnv4_module_forward_noalloc(const void* x_in, const dcnv4_module_weights* w, void* out,
+                                 int N, int H, int W, const dcnv4_module_config* cfg, int dtype, void* stream)
+{
+    ModuleLayout L;
+    const int st = validate_config(N, H, W, cfg, dtype, &L);
+    if (st != DCNV4_OK) return st;
+    if (L.total > (int64_t)DCNV4_MODULE_SCRATCH_BYTES)
+        return fail(DCNV4_ERR_TOO_LARGE, "the problem needs a %lld-byte workspace; the no-allocation variant holds "
+                    "%lld bytes (use dcnv4_module_forward with a workspace)", (long long)L.total,
+                    (long long)DCNV4_MODULE_SCRATCH_BYTES);
+    if (N == 0) return DCNV4_OK;
+    int cus = 0;
+    const int dst = dcnv4::check_device(&cus);
+    if (dst != DCNV4_OK) return dst;
+    void* ws = scratch_address();
+    if (!ws) return DCNV4_ERR_HIP;
+    return module_forward_impl(x_in, w, out, N, H, W, cfg, ws, (size_t)DCNV4_MODULE_SCRATCH_BYTES, dtype, stream,
+                               L);
 }
 
 }  // extern "C"

@@ -42,8 +42,8 @@
  * Weights: the matrices (w_in, w_pred, w_out) in the I/O type, row-major
  * [out, in]; every vector and the depthwise taps in binary32.  All pointers
  * are device pointers owned by the caller.  The intermediate tensors live in
- * a caller-owned workspace (dcnv4_module_workspace_bytes; layout below, so
- * that a caller may read them), which the call overwrites; the call
+ * a caller-owned workspace (dcnv4_module_workspace_layout gives its size and
+ * layout, so that a caller may read them), which the call overwrites; the call
  * allocates nothing.  Enqueued on `stream`, no synchronisation; validation
  * before any HIP call, as in dcnv4.h.
  */
@@ -114,6 +114,26 @@ int dcnv4_module_workspace_layout(int N, int H, int W, const dcnv4_module_config
 int dcnv4_module_forward(const void* x_in, const dcnv4_module_weights* weights, void* out,
                          int N, int H, int W, const dcnv4_module_config* cfg,
                          void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * module forward, its intermediates held in a library-owned device array of
+ * DCNV4_MODULE_SCRATCH_BYTES per GPU instead of a workspace argument.  The
+ * array is part of the library's code object (each GPU the library runs on
+ * holds it until the process ends); the call allocates and frees nothing.
+ * A problem whose workspace (dcnv4_module_workspace_layout's total) exceeds
+ * the array is rejected with DCNV4_ERR_TOO_LARGE before any HIP call.  Every
+ * call on a GPU uses that GPU's one array and leaves its intermediates there
+ * (no step reads a part of it that the same call has not written first):
+ * calls that overlap on one GPU (two streams, two host threads) race, and
+ * the caller must order them.  Other arguments and errors as for
+ * dcnv4_module_forward.
+ */
+#define DCNV4_MODULE_SCRATCH_BYTES ((size_t)64 << 20)
+
+int dcnv4_module_forward_noalloc(const void* x_in, const dcnv4_module_weights* weights, void* out,
+                                 int N, int H, int W, const dcnv4_module_config* cfg, int dtype, void* stream);
 
 #ifdef __cplusplus
 }
