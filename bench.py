@@ -116,9 +116,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="fiit_stage1")
-    ap.add_argument("--op", default="forward", choices=("forward", "backward", "softmax"),
-                    help="forward (the headline), the backward (gradients of x, offsets, weights), or "
-                         "softmax (the DCNv3-style aggregation, for comparison)")
+    ap.add_argument("--op", default="forward", choices=("forward", "backward", "softmax", "module"),
+                    help="forward (the headline), the backward (gradients of x, offsets, weights), "
+                         "softmax (the DCNv3-style aggregation, for comparison), or module (the module "
+                         "forward around the operator: projection, group norm, predictor, operator, "
+                         "centre gate, output projection, C in and out)")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's last)")
     ap.add_argument("--batch", type=int, default=None,
                     help="run the workload's shape at this batch size instead of its own")
@@ -259,6 +261,8 @@ def main():
         torch.cuda.empty_cache()
         return r
 
+    if args.op == "module":
+        return bench_module(args, wl, dtype, log)
     r = measure(wl, dtype, args.op, args.steps, args.warmup, args.rotate_bytes)
     x, off, m = r["inputs"]
     alg_bytes = wl.backward_bytes(dtype) if args.op == "backward" else wl.algorithmic_bytes(dtype)
@@ -343,6 +347,90 @@ def main():
         },
         "configs": configs,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def module_bytes(wl, dtype):
+    """The module's compulsory traffic: x_in read once and out written once
+    (C channels each), plus the weights (matrices in the I/O type, vectors in
+    binary32)."""
+    s = 4 if dtype == "f32" else 2
+    C, P, G = wl.C, wl.P, wl.G
+    R = 3 * G * P + G
+    px = wl.N * wl.H * wl.W
+    return 2 * px * C * s + (C * C + R * C + C * C) * s + (4 * C + 9 * C + R + C) * 4
+
+
+def bench_module(args, wl, dtype, log):
+    """Time the module forward (group norm over min(32, C) groups, centre gate,
+    output projection; Cin = Cout = C) on seeded random weights."""
+    import numpy as np
+    import torch
+
+    from deformable_convolution_vision_dcnv4_amd import binding
+    from deformable_convolution_vision_dcnv4_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    C, G, P = wl.C, wl.G, wl.P
+    R = 3 * G * P + G
+    rng = np.random.default_rng(wl.seed)
+
+    def mat(shape, std):
+        h = gen.to_io(rng.standard_normal(shape) * std, dtype)
+        if dtype == "bf16":
+            return torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(h).to(dev)
+
+    def vec(shape, std, mean=0.0):
+        return torch.from_numpy((mean + rng.standard_normal(shape) * std).astype(np.float32)).to(dev)
+
+    scale = np.concatenate([np.full(2 * G * P, 1.5), np.full(G * P, 0.5), np.full(G, 1.0)])[:, None]
+    w_pred = gen.to_io(rng.standard_normal((R, C)) * scale / np.sqrt(C), dtype)
+    weights = {"w_in": mat((C, C), 1 / np.sqrt(C)), "b_in": vec(C, 0.1), "gamma": vec(C, 0.1, 1.0),
+               "beta": vec(C, 0.1), "w_dw": vec((C, 3, 3), 1 / 3), "b_dw": vec(C, 0.05),
+               "w_pred": (torch.from_numpy(w_pred.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
+                          else torch.from_numpy(w_pred)).to(dev),
+               "b_pred": vec(R, 0.1), "w_out": mat((C, C), 1 / np.sqrt(C)), "b_out": vec(C, 0.1)}
+    cfg = binding.module_config(Cin=C, G=G, Cg=wl.Cg, Cout=C, norm=binding.NORM_GROUP, norm_groups=min(32, C),
+                                eps=1e-5, center_scale=True, out_proj=True)
+    log(f"module on {wl.describe(dtype)}: generating inputs")
+    x = gen.to_io(gen.draw(wl.seed, gen.STREAM_X, wl.N * wl.H * wl.W * C, wl.x_dist), dtype)
+    xs = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
+          else torch.from_numpy(x)).to(dev).reshape(wl.N, wl.H, wl.W, C)
+    lay = binding.module_layout(wl.N, wl.H, wl.W, cfg, tdt)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.N, wl.H, wl.W, C), dtype=tdt, device=dev)
+    for _ in range(args.warmup):
+        binding.module_forward(xs, weights, cfg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        binding.module_forward(xs, weights, cfg, out=out, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    alg = module_bytes(wl, dtype)
+    log(f"timed {args.steps} module forwards: {ms * 1e3:.2f} us each (events), workspace {lay['total'] / 2**20:.1f} MiB")
+    ms_step = wall * 1e3 / args.steps
+    rec = {
+        "metric": "DCNv4 module fwd GB/s per MI355X (x in + out + weights); % of HBM roofline",
+        "value": round(alg / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded inputs and random weights; no dataset, no trained weights)",
+        "config": {"workload": wl.describe(dtype), "op": "module", "norm": "group", "norm_groups": min(32, C),
+                   "center_scale": True, "out_proj": True, "Cin": C, "Cout": C,
+                   "algorithmic_bytes_per_step": alg, "workspace_bytes": lay["total"]},
+        "kernel_us_mean": round(ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
 

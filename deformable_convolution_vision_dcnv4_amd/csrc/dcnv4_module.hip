@@ -90,14 +90,27 @@ template <> struct Mfma<DCNV4_F32> {
     }
 };
 
-// Column blocks of 16 per pass (accumulators held: 4 registers each).
+// Column blocks of 16 per pass (accumulators held: 4 registers each), and
+// the k chunk of the weight tile staged in LDS per step of the pass.
 constexpr int kGemmBlocks = 8;
+constexpr int kGemmCols = 16 * kGemmBlocks;
+template <int DT> constexpr int kGemmKc = DT == DCNV4_F32 ? 32 : 64;
+// LDS row pitch of the weight tile (elements): rows 4 (f32) or 8 (16-bit)
+// bytes longer than the chunk, so that the 16 lanes reading one fragment
+// column from 16 rows fall on different banks.
+template <int DT> constexpr int kGemmPitch = kGemmKc<DT> + (DT == DCNV4_F32 ? 1 : 4);
+constexpr int kGemmOutPitch = kGemmCols + 2;
 
 // out[m][n] = round(sum_k a[m][k] * w[n][k] + bias[n]) for m < M, n < Nn.
 // a: rows of lda elements (K used), w: [Nn][K] dense, out: rows of ldo.
-// K is a multiple of 4 (16-bit: the fragments are 8-byte loads).  Reads past
-// a row's K-th element or past the last row/column return zero (buffer range
-// checks on the resources below), so ragged edges need no branches.
+// A workgroup of 4 waves takes 64 rows; per pass of 128 columns the weight
+// tile goes through LDS in k chunks (each weight element read once per
+// workgroup and pass), each wave reads its 16 rows' fragments from global
+// memory (a chunk's loads issued together), and the results are gathered in
+// LDS per wave and written row by row, consecutive lanes on consecutive
+// columns.  K is a multiple of 4 for 16-bit types (8-byte loads).  Reads past
+// a row's K-th element or past the last row or column return zero (buffer
+// range checks), so ragged edges need no branches in the main loop.
 template <int DT>
 __global__ void __launch_bounds__(256) k_gemm(const void* __restrict__ a, int64_t lda, const void* __restrict__ w,
                                               const float* __restrict__ bias, void* __restrict__ out, int64_t ldo,
@@ -105,51 +118,84 @@ __global__ void __launch_bounds__(256) k_gemm(const void* __restrict__ a, int64_
 {
     using MF = Mfma<DT>;
     using E = Elem<DT>;
+    using S = typename E::S;
     constexpr int s = E::kBytes;
-    const uint32_t lane = threadIdx.x & 63u;
-    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
-    if (row0 >= M) return;
-    const int rows_here = (int)min<int64_t>(16, M - row0);
-    // this wave's 16 rows of a, and all of w; the k range checks by resource size
-    // happen per row below (k >= K reads zero through the per-lane offset test)
-    const char* abase = static_cast<const char*>(a) + row0 * lda * s;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint32_t)(((int64_t)(rows_here - 1) * lda + K) * s));
+    constexpr int KC = kGemmKc<DT>, WP = kGemmPitch<DT>;
+    constexpr int STEPS = KC / MF::kK;
+    __shared__ S wt[kGemmCols * WP];
+    __shared__ S ot[4][16 * kGemmOutPitch];
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const int64_t row0 = (int64_t)blockIdx.x * 64 + wave * 16;
+    const int rows_here = row0 < M ? (int)min<int64_t>(16, M - row0) : 0;
+    const char* abase = static_cast<const char*>(a) + (rows_here ? row0 : 0) * lda * s;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(abase, rows_here ? (uint32_t)(((int64_t)(rows_here - 1) * lda + K) * s) : 0u);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)Nn * K * s));
     const uint32_t li = lane & 15u, lk = lane >> 4;      // row (or column) and k group of this lane
     const int kq = MF::kPer * (int)lk;                     // first k of this lane in a step
-    for (int n0 = 0; n0 < Nn; n0 += 16 * kGemmBlocks) {
+    constexpr int EPL = DT == DCNV4_F32 ? 1 : 4;           // elements per staging load
+    for (int n0 = 0; n0 < Nn; n0 += kGemmCols) {
         f4 acc[kGemmBlocks];
 #pragma unroll
         for (int b = 0; b < kGemmBlocks; ++b) acc[b] = f4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < K; k0 += MF::kK) {
-            const int k = k0 + kq;
-            // a row past the wave's last, or a k past K: zeros
-            const bool ain = ((int)li < rows_here) & (k < K);
-            const uint32_t aoff = ain ? (uint32_t)(((int64_t)li * lda + k) * s) : kOobOffset;
-            const typename MF::Frag fa = MF::load(ra, aoff);
+        for (int kc0 = 0; kc0 < K; kc0 += KC) {
+            // this wave's A fragments of the chunk, requested before the tile
+            typename MF::Frag fa[STEPS];
 #pragma unroll
-            for (int b = 0; b < kGemmBlocks; ++b) {
-                const int n = n0 + 16 * b + (int)li;
-                const bool win = (n < Nn) & (k < K);
-                const uint32_t woff = win ? (uint32_t)(((int64_t)n * K + k) * s) : kOobOffset;
-                acc[b] = MF::mma(fa, MF::load(rw, woff), acc[b]);
+            for (int st = 0; st < STEPS; ++st) {
+                const int k = kc0 + st * MF::kK + kq;
+                const bool ain = ((int)li < rows_here) & (k < K);
+                fa[st] = MF::load(ra, ain ? (uint32_t)(((int64_t)li * lda + k) * s) : kOobOffset);
+            }
+            __syncthreads();   // the previous chunk's tile is consumed
+            for (int e = threadIdx.x * EPL; e < kGemmCols * KC; e += 256 * EPL) {
+                const int r = e / KC, c = e - r * KC;
+                const int n = n0 + r, k = kc0 + c;
+                const bool in = (n < Nn) & (k < K);
+                const uint32_t off = in ? (uint32_t)(((int64_t)n * K + k) * s) : kOobOffset;
+                if constexpr (EPL == 4) {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)off, 0, 0);
+                    *reinterpret_cast<u32x2*>(&wt[r * WP + c]) = v;
+                } else {
+                    wt[r * WP + c] = __builtin_bit_cast(S, __builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0));
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+#pragma unroll
+                for (int b = 0; b < kGemmBlocks; ++b) {
+                    if (n0 + 16 * b >= Nn) break;   // (uniform) no column of this block exists
+                    const S* src = &wt[(16 * b + li) * WP + st * MF::kK + kq];
+                    typename MF::Frag fb;
+                    if constexpr (EPL == 4)
+                        fb = __builtin_bit_cast(typename MF::Frag, *reinterpret_cast<const u32x2*>(src));
+                    else
+                        fb = *src;
+                    acc[b] = MF::mma(fa[st], fb, acc[b]);
+                }
             }
         }
+        // bias, one rounding, through this wave's LDS tile to row-wise stores
+        const int ncols = min(kGemmCols, Nn - n0);
 #pragma unroll
         for (int b = 0; b < kGemmBlocks; ++b) {
-            const int n = n0 + 16 * b + (int)li;
-            if (n >= Nn) continue;
-            const float bn = bias[n];
+            const int col = 16 * b + (int)li;
+            if (col >= ncols) continue;
+            const float bn = bias[n0 + col];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * (int)lk + r;
-                if (row >= rows_here) continue;
-                const float v = acc[b][r] + bn;
-                typename E::S* o = reinterpret_cast<typename E::S*>(static_cast<char*>(out) +
-                                                                     ((row0 + row) * ldo + n) * s);
-                *o = E::from_f(v);
-            }
+            for (int r = 0; r < 4; ++r) ot[wave][(4 * (int)lk + r) * kGemmOutPitch + col] = E::from_f(acc[b][r] + bn);
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int r = 0; r < rows_here; ++r) {
+            S* orow = static_cast<S*>(out) + (row0 + r) * ldo + n0;
+            for (int c = (int)lane; c < ncols; c += 64) orow[c] = ot[wave][r * kGemmOutPitch + c];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -226,68 +272,139 @@ __global__ void __launch_bounds__(256) k_gn_finalize(const double* __restrict__ 
     stat[i * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
 }
 
-// xn = round((xp - mean) * rstd * gamma + beta): one wave per pixel.  Group
-// norm: (mean, rstd) of the channel's group from `stat`; layer norm: computed
-// here from the pixel's C channels (binary64 sums, lanes then a butterfly).
-template <int DT, int LAYER>
+// VE consecutive elements of the I/O type as binary32 (VE = 1, or one
+// 16-byte vector), and back with one rounding each.
+template <int DT, int VE>
+__device__ __forceinline__ void load_vals(const void* p, float* v)
+{
+    using E = Elem<DT>;
+    if constexpr (VE == 1) {
+        v[0] = E::to_f(*static_cast<const typename E::S*>(p));
+    } else {
+        static_assert(VE == kPerVec<DT>, "one 16-byte vector");
+        const u32x4 q = *static_cast<const u32x4*>(p);
+        const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == DCNV4_F32) {
+                v[i] = __uint_as_float(d[i]);
+            } else {
+                v[2 * i] = E::raw_to_f(d[i] & 0xffffu);
+                v[2 * i + 1] = E::raw_to_f(d[i] >> 16);
+            }
+        }
+    }
+}
+
+template <int DT, int VE>
+__device__ __forceinline__ void store_vals(void* p, const float* v)
+{
+    using E = Elem<DT>;
+    if constexpr (VE == 1) {
+        *static_cast<typename E::S*>(p) = E::from_f(v[0]);
+    } else {
+        *static_cast<u32x4*>(p) = pack_vec16<DT>(v);
+    }
+}
+
+// xn = round((xp - mean) * rstd * gamma + beta), VE channels per thread.
+// Group norm: (mean, rstd) of each channel's group from `stat`, one thread
+// per (pixel, VE channels).  Layer norm: the pixel's statistics computed
+// here by a segment of lpp lanes (a power of two covering its C / VE chunks;
+// 64 / lpp pixels per wave), binary64 sums, butterflies within the segment.
+template <int DT, int LAYER, int VE>
 __global__ void __launch_bounds__(256) k_norm(const void* __restrict__ xp, void* __restrict__ xn,
                                               const float* __restrict__ stat, const float* __restrict__ gamma,
                                               const float* __restrict__ beta, int64_t npix, int HW, int C,
-                                              int groups, float eps)
+                                              int groups, float eps, int lpp)
 {
     using E = Elem<DT>;
-    const int64_t pix = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pix >= npix) return;
-    const int lane = threadIdx.x & 63;
-    const typename E::S* x = static_cast<const typename E::S*>(xp) + pix * C;
-    typename E::S* o = static_cast<typename E::S*>(xn) + pix * C;
-    float mean = 0.f, rstd = 0.f;
-    if (LAYER) {
-        double s1 = 0.0, s2 = 0.0;
-        for (int c = lane; c < C; c += 64) {
-            const double v = (double)E::to_f(x[c]);
-            s1 += v;
-            s2 += v * v;
+    constexpr int s = E::kBytes;
+    const int chunks = C / VE;
+    if (!LAYER) {
+        const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (i >= npix * chunks) return;
+        const int64_t pix = i / chunks;
+        const int c0 = (int)(i - pix * chunks) * VE;
+        const int n = (int)(pix / HW), cpg = C / groups;
+        float v[VE];
+        load_vals<DT, VE>(static_cast<const char*>(xp) + (pix * C + c0) * s, v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            const float* st = stat + ((int64_t)n * groups + (c0 + e) / cpg) * 2;
+            v[e] = fmaf((v[e] - st[0]) * st[1], gamma[c0 + e], beta[c0 + e]);
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            s1 += __shfl_xor(s1, off);
-            s2 += __shfl_xor(s2, off);
-        }
-        const double m = s1 / C;
-        double var = s2 / C - m * m;
-        var = var > 0.0 ? var : 0.0;
-        mean = (float)m;
-        rstd = (float)(1.0 / sqrt(var + (double)eps));
+        store_vals<DT, VE>(static_cast<char*>(xn) + (pix * C + c0) * s, v);
+        return;
     }
-    const int n = (int)(pix / HW), cpg = C / groups;
-    for (int c = lane; c < C; c += 64) {
-        if (!LAYER) {
-            const float* st = stat + ((int64_t)n * groups + c / cpg) * 2;
-            mean = st[0];
-            rstd = st[1];
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & (lpp - 1);
+    const int64_t pix = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / lpp) + lane / lpp;
+    const bool live = pix < npix;
+    const char* x = static_cast<const char*>(xp) + (live ? pix : 0) * C * s;
+    double s1 = 0.0, s2 = 0.0;
+    if (live) {
+        for (int j = sub; j < chunks; j += lpp) {
+            float v[VE];
+            load_vals<DT, VE>(x + (int64_t)j * VE * s, v);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                s1 += (double)v[e];
+                s2 += (double)v[e] * (double)v[e];
+            }
         }
-        const float v = (E::to_f(x[c]) - mean) * rstd;
-        o[c] = E::from_f(fmaf(v, gamma[c], beta[c]));
+    }
+    for (int off = lpp >> 1; off >= 1; off >>= 1) {
+        s1 += __shfl_xor(s1, off);
+        s2 += __shfl_xor(s2, off);
+    }
+    if (!live) return;
+    const double m = s1 / C;
+    double var = s2 / C - m * m;
+    var = var > 0.0 ? var : 0.0;
+    const float mean = (float)m, rstd = (float)(1.0 / sqrt(var + (double)eps));
+    char* o = static_cast<char*>(xn) + pix * C * s;
+    for (int j = sub; j < chunks; j += lpp) {
+        float v[VE];
+        load_vals<DT, VE>(x + (int64_t)j * VE * s, v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[e] = fmaf((v[e] - mean) * rstd, gamma[j * VE + e], beta[j * VE + e]);
+        store_vals<DT, VE>(o + (int64_t)j * VE * s, v);
     }
 }
 
 // d = round(b[c] + sum_{i,j} w[c][i][j] * xn[h + i - 1][w + j - 1][c]), zero
-// padding; one thread per element.
-template <int DT>
+// padding, taps in row-major order; one thread per (pixel, VE channels).
+// LDSW: the taps and biases are first copied to LDS (C * 10 floats), so that
+// each thread's 9 * VE tap reads are LDS reads rather than global loads.
+template <int DT, int VE, int LDSW>
 __global__ void __launch_bounds__(256) k_dw3x3(const void* __restrict__ xn, void* __restrict__ d,
                                                const float* __restrict__ w, const float* __restrict__ b,
                                                int N, int H, int W, int C)
 {
     using E = Elem<DT>;
+    constexpr int s = E::kBytes;
+    extern __shared__ float wl[];
+    const float* wt = w;
+    const float* bt = b;
+    if (LDSW) {
+        for (int i = threadIdx.x; i < C * 9; i += blockDim.x) wl[i] = w[i];
+        for (int i = threadIdx.x; i < C; i += blockDim.x) wl[C * 9 + i] = b[i];
+        __syncthreads();
+        wt = wl;
+        bt = wl + C * 9;
+    }
+    const int chunks = C / VE;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)N * H * W * C;
-    if (i >= total) return;
-    const int c = (int)(i % C);
-    const int64_t pix = i / C;
+    if (i >= (int64_t)N * H * W * chunks) return;
+    const int64_t pix = i / chunks;
+    const int c0 = (int)(i - pix * chunks) * VE;
     const int wx = (int)(pix % W), hy = (int)((pix / W) % H);
     const int64_t img = pix / ((int64_t)H * W);
-    const typename E::S* x = static_cast<const typename E::S*>(xn) + img * H * W * C;
-    float acc = b[c];
+    const char* x = static_cast<const char*>(xn) + (img * H * W * C + c0) * s;
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = bt[c0 + e];
 #pragma unroll
     for (int ii = 0; ii < 3; ++ii) {
         const int y = hy + ii - 1;
@@ -296,28 +413,41 @@ __global__ void __launch_bounds__(256) k_dw3x3(const void* __restrict__ xn, void
         for (int jj = 0; jj < 3; ++jj) {
             const int xx = wx + jj - 1;
             if (xx < 0 || xx >= W) continue;
-            acc = fmaf(w[c * 9 + ii * 3 + jj], E::to_f(x[((int64_t)y * W + xx) * C + c]), acc);
+            float v[VE];
+            load_vals<DT, VE>(x + ((int64_t)y * W + xx) * C * s, v);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] = fmaf(wt[(c0 + e) * 9 + ii * 3 + jj], v[e], acc[e]);
         }
     }
-    static_cast<typename E::S*>(d)[i] = E::from_f(acc);
+    store_vals<DT, VE>(static_cast<char*>(d) + (pix * C + c0) * s, acc);
 }
 
-// gated = round(y * (1 - s) + xn * s), s = sigmoid(rows[pix][gate0 + c / Cg]).
-template <int DT>
+// gated = round(y * (1 - s) + xn * s), s = sigmoid(rows[pix][gate0 + c / Cg]);
+// one thread per (pixel, VE channels).
+template <int DT, int VE>
 __global__ void __launch_bounds__(256) k_gate(const void* __restrict__ y, const void* __restrict__ xn,
                                               const void* __restrict__ rows, int64_t rstride, int gate0,
                                               void* __restrict__ out, int64_t npix, int C, int Cg)
 {
     using E = Elem<DT>;
+    constexpr int s = E::kBytes;
+    const int chunks = C / VE;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= npix * C) return;
-    const int64_t pix = i / C;
-    const int c = (int)(i % C);
-    const float t = E::to_f(static_cast<const typename E::S*>(rows)[pix * rstride + gate0 + c / Cg]);
-    const float sg = 1.0f / (1.0f + expf(-t));
-    const float yv = E::to_f(static_cast<const typename E::S*>(y)[i]);
-    const float xv = E::to_f(static_cast<const typename E::S*>(xn)[i]);
-    static_cast<typename E::S*>(out)[i] = E::from_f(yv * (1.0f - sg) + xv * sg);
+    if (i >= npix * chunks) return;
+    const int64_t pix = i / chunks;
+    const int c0 = (int)(i - pix * chunks) * VE;
+    const int64_t at = (pix * C + c0) * s;
+    float yv[VE], xv[VE];
+    load_vals<DT, VE>(static_cast<const char*>(y) + at, yv);
+    load_vals<DT, VE>(static_cast<const char*>(xn) + at, xv);
+    const typename E::S* lg = static_cast<const typename E::S*>(rows) + pix * rstride + gate0;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        const float t = E::to_f(lg[(c0 + e) / Cg]);
+        const float sg = 1.0f / (1.0f + expf(-t));
+        yv[e] = yv[e] * (1.0f - sg) + xv[e] * sg;
+    }
+    store_vals<DT, VE>(static_cast<char*>(out) + at, yv);
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -334,6 +464,10 @@ hipError_t run(const ModuleProblem& m, hipStream_t st)
     void* d = ws + L.d;
     void* rows = ws + L.rows;
     const int64_t gblocks = cdiv(npix, 64);
+    // elementwise steps: one 16-byte vector per thread when the channels
+    // split into whole vectors (the workspace regions are 256-byte aligned)
+    constexpr int VE = kPerVec<DT>;
+    const bool vec = C % VE == 0 && (uintptr_t)m.out % 16 == 0;
     // 1. projection
     hipLaunchKernelGGL(k_gemm<DT>, dim3((unsigned)gblocks), dim3(256), 0, st, m.x_in, (int64_t)m.Cin, m.w.w_in,
                        m.w.b_in, xp, (int64_t)C, npix, m.Cin, C);
@@ -345,15 +479,44 @@ hipError_t run(const ModuleProblem& m, hipStream_t st)
                            L.slices);
         hipLaunchKernelGGL(k_gn_finalize, dim3((unsigned)cdiv((int64_t)m.N * m.norm_groups, 256)), dim3(256), 0, st,
                            part, stat, m.N, HW, C, m.norm_groups, L.slices, m.eps);
-        hipLaunchKernelGGL((k_norm<DT, 0>), dim3((unsigned)cdiv(npix, 4)), dim3(256), 0, st, xp, xn, stat,
-                           m.w.gamma, m.w.beta, npix, HW, C, m.norm_groups, m.eps);
+        if (vec)
+            hipLaunchKernelGGL((k_norm<DT, 0, VE>), dim3((unsigned)cdiv(npix * (C / VE), 256)), dim3(256), 0, st, xp,
+                               xn, stat, m.w.gamma, m.w.beta, npix, HW, C, m.norm_groups, m.eps, 1);
+        else
+            hipLaunchKernelGGL((k_norm<DT, 0, 1>), dim3((unsigned)cdiv(npix * C, 256)), dim3(256), 0, st, xp, xn,
+                               stat, m.w.gamma, m.w.beta, npix, HW, C, m.norm_groups, m.eps, 1);
     } else if (m.norm == DCNV4_NORM_LAYER) {
-        hipLaunchKernelGGL((k_norm<DT, 1>), dim3((unsigned)cdiv(npix, 4)), dim3(256), 0, st, xp, xn, nullptr,
-                           m.w.gamma, m.w.beta, npix, HW, C, 1, m.eps);
+        // a segment of lpp lanes (a power of two, at most 64) per pixel
+        const int chunks = vec ? C / VE : C;
+        int lpp = 1;
+        while (lpp < chunks && lpp < 64) lpp <<= 1;
+        const unsigned grid = (unsigned)cdiv(npix, 4 * (64 / lpp));
+        if (vec)
+            hipLaunchKernelGGL((k_norm<DT, 1, VE>), dim3(grid), dim3(256), 0, st, xp, xn, nullptr, m.w.gamma,
+                               m.w.beta, npix, HW, C, 1, m.eps, lpp);
+        else
+            hipLaunchKernelGGL((k_norm<DT, 1, 1>), dim3(grid), dim3(256), 0, st, xp, xn, nullptr, m.w.gamma,
+                               m.w.beta, npix, HW, C, 1, m.eps, lpp);
     }
     // 3. depthwise 3x3, 4. predictor
-    hipLaunchKernelGGL(k_dw3x3<DT>, dim3((unsigned)cdiv(npix * C, 256)), dim3(256), 0, st, xn, d, m.w.w_dw,
-                       m.w.b_dw, m.N, m.H, m.W, C);
+    {
+        // taps through LDS when they fit in 64 KiB (up to 1638 channels)
+        const size_t wbytes = (size_t)C * 10 * sizeof(float);
+        const bool lw = wbytes <= 64 * 1024;
+        const unsigned grid = (unsigned)cdiv(npix * (vec ? C / VE : C), 256);
+        if (vec && lw)
+            hipLaunchKernelGGL((k_dw3x3<DT, VE, 1>), dim3(grid), dim3(256), wbytes, st, xn, d, m.w.w_dw, m.w.b_dw,
+                               m.N, m.H, m.W, C);
+        else if (vec)
+            hipLaunchKernelGGL((k_dw3x3<DT, VE, 0>), dim3(grid), dim3(256), 0, st, xn, d, m.w.w_dw, m.w.b_dw, m.N,
+                               m.H, m.W, C);
+        else if (lw)
+            hipLaunchKernelGGL((k_dw3x3<DT, 1, 1>), dim3(grid), dim3(256), wbytes, st, xn, d, m.w.w_dw, m.w.b_dw,
+                               m.N, m.H, m.W, C);
+        else
+            hipLaunchKernelGGL((k_dw3x3<DT, 1, 0>), dim3(grid), dim3(256), 0, st, xn, d, m.w.w_dw, m.w.b_dw, m.N,
+                               m.H, m.W, C);
+    }
     hipLaunchKernelGGL(k_gemm<DT>, dim3((unsigned)gblocks), dim3(256), 0, st, d, (int64_t)C, m.w.w_pred,
                        m.w.b_pred, rows, L.rows_stride, npix, C, L.R);
     hipError_t e = hipGetLastError();
@@ -386,8 +549,12 @@ hipError_t run(const ModuleProblem& m, hipStream_t st)
     void* last = y;
     if (m.center_scale) {
         void* g = L.gated >= 0 ? ws + L.gated : m.out;
-        hipLaunchKernelGGL(k_gate<DT>, dim3((unsigned)cdiv(npix * C, 256)), dim3(256), 0, st, y, xn, rows,
-                           L.rows_stride, 3 * m.G * L.P, g, npix, C, m.Cg);
+        if (vec)
+            hipLaunchKernelGGL((k_gate<DT, VE>), dim3((unsigned)cdiv(npix * (C / VE), 256)), dim3(256), 0, st, y, xn,
+                               rows, L.rows_stride, 3 * m.G * L.P, g, npix, C, m.Cg);
+        else
+            hipLaunchKernelGGL((k_gate<DT, 1>), dim3((unsigned)cdiv(npix * C, 256)), dim3(256), 0, st, y, xn, rows,
+                               L.rows_stride, 3 * m.G * L.P, g, npix, C, m.Cg);
         last = g;
     }
     if (m.out_proj)
