@@ -41,6 +41,7 @@ struct Plan {
     int lds_bytes;  // dynamic LDS (window)
     int lds_total;  // all LDS per workgroup (the coalesced variant adds static buffers)
     int lpu;        // window: lanes per unit (> 1: one 16-byte vector per lane)
+    int share;      // window: split units share their points' coefficients (2 or 4 lanes)
 };
 
 // Largest LDS allocation one workgroup may use on gfx950 (the CU's 160 KiB).

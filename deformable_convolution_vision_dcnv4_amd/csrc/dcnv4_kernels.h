@@ -71,6 +71,7 @@ struct KArgs {
     uint32_t lds_bytes;             // all dynamic LDS
     int lpu;                        // lanes per unit (> 1: one 16-byte vector per lane)
     int nvt;                        // 16-byte vectors per unit
+    int share;                      // split units of 2 or 4 lanes share point coefficients
     FastDiv div_lpu;
 };
 

@@ -32,7 +32,7 @@
 // DCNV4_TUNE (environment, parsed again whenever its text changes)
 // overrides the choices for tuning runs and tests; an explicit kernel, tile
 // height or width, group count or full=0|1 turns the GPU-filling rule off:
-// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1,pitch_add=E,coal=0|1,split=0|1".
+// "kernel=direct|window,gb=G,th=T,tw=T,r=R,block=B,full=0|1,pitch_add=E,coal=0|1,split=0|1,share=0|1".
 
 #include <stdio.h>
 #include <stdlib.h>
@@ -49,6 +49,7 @@ namespace {
 struct Tune {
     int kernel = 0;     // 0 auto, 1 direct, 2 window
     int gb = 0, th = 0, tw = 0, r = -1, block = 0, full = -1, pitch_add = 0, coal = -1, split = -1;
+    int share = -1;          // split units of 2 or 4 lanes share point coefficients
 };
 
 // Parsed per thread, again whenever the variable's text changes.
@@ -82,6 +83,7 @@ const Tune& tune()
             else if (!strcmp(tok, "pitch_add")) t.pitch_add = atoi(v);
             else if (!strcmp(tok, "coal")) t.coal = atoi(v);
             else if (!strcmp(tok, "split")) t.split = atoi(v);
+            else if (!strcmp(tok, "share")) t.share = atoi(v);
         }
     }
     return t;
@@ -244,6 +246,10 @@ bool plan_window(const Problem& p, Plan* pl)
     pl->vec = 16;
     pl->lanes = lpu;
     pl->lpu = lpu;
+    // point coefficients shared over a unit's lanes: four lanes (stage-1 fp32:
+    // 70.9-78.9 us against 75.6-79.7 without); two lanes measured slower
+    // (the 256x256 bf16 shape: 136.7 against 123.6 us), so only on request
+    pl->share = (lpu == 4 && t.share != 0) || (lpu == 2 && t.share == 1) ? 1 : 0;
     pl->block = block;
     pl->nv = nv;
     pl->GB = GB; pl->TH = TH; pl->TW = TW; pl->RY = full ? 0 : R; pl->RX = full ? 0 : R;
@@ -273,6 +279,7 @@ void plan_direct(const Problem& p, Plan* pl)
     pl->lds_total = 0;
     pl->lds_bytes = 0;
     pl->lpu = 1;
+    pl->share = 0;
     const int64_t lanes_img = (int64_t)p.Ho * p.Wo * p.G * pl->lanes;
     pl->grid = (int64_t)p.N * ceil_div(lanes_img, 256);
 }
@@ -337,6 +344,7 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
     a.win_bytes = (uint32_t)plan.lds_bytes;
     a.lds_bytes = (uint32_t)plan.lds_total;
     a.lpu = plan.lpu;
+    a.share = plan.share;
     a.nvt = plan.nv;
     a.div_lpu = make_fastdiv((uint32_t)plan.lpu);
     return launch_window(a, p.dtype, plan.nv, plan.block, plan.grid, stream);

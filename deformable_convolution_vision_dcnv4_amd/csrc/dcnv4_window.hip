@@ -114,6 +114,16 @@ __device__ __forceinline__ void pin(PointRegs<NV>& r)
     }
 }
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 // Index of the n-th (from 0) set bit of m; n < popcount(m).
 __device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, int n)
 {
@@ -274,15 +284,121 @@ __device__ __forceinline__ void unit_global(float* acc, const WinCtx& x, const R
     }
 }
 
+// Units split over SH lanes (SH = 2 or 4, so that a unit's lanes sit in one
+// quad of lanes): the unit's P points are dealt to its lanes, lane v taking
+// points v, v + SH, ...; each lane computes position, weights and corner
+// address of its points only, and every point's are then broadcast to the
+// unit's lanes with a quad permutation (DPP), instead of every lane
+// computing all P points.  The operations and their order are the same as
+// in issue_point, so the results are the same bits.
+struct SlotCoef {
+    float w00, w01, w10, w11;
+    int a00;            // LDS byte of corner 00 for vector 0 of the unit
+};
+
+// Element e of a row when e depends on the lane: one of the SH candidates
+// base .. base + SH - 1 (clamped to the row), chosen by v.
+// (Each candidate passes through an empty asm: otherwise the optimiser turns
+// the chain of selects into one load with a lane-dependent index, which puts
+// the row in scratch memory.)
+template <int SH, int DT, int NE>
+__device__ __forceinline__ float row_pick(const RowLoad<DT, NE>& r, int base, int v)
+{
+    float x = r.get(base < NE ? base : NE - 1);
+    asm volatile("" : "+v"(x));
+#pragma unroll
+    for (int t = 1; t < SH; ++t) {
+        const int e = base + t < NE ? base + t : NE - 1;
+        float y = r.get(e);
+        asm volatile("" : "+v"(y));
+        x = v == t ? y : x;
+    }
+    return x;
+}
+
+// Slot s of this lane (point k = s * SH + v): the steps of issue_point up to
+// the corner address; `live` is false for a k past the unit's points.
+template <int DT, int FULL, int RC, int P, int SH, int S>
+__device__ __forceinline__ SlotCoef slot_coef(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
+                                              const RowLoad<DT, P>& msk, int v, int bx, int by, int ubase,
+                                              bool& fb)
+{
+    constexpr int s = S;
+    const int k = s * SH + v;
+    const bool live = k < P;
+    const int q = k + ((RC && k >= 4) ? 1 : 0);
+    const int i = (q * 11) >> 5, j = q - 3 * i;          // q / 3 and q % 3 for q < 10
+    float px = fmaf(row_pick<SH>(offs, s * SH, v), x.scale, (float)(bx + j * x.dil));
+    float py = fmaf(row_pick<SH>(offs, P + s * SH, v), x.scale, (float)(by + i * x.dil));
+    float m = row_pick<SH>(msk, s * SH, v);
+    const bool valid = (px > -1.0f) & (px < x.fW) & (py > -1.0f) & (py < x.fH);
+    bool ok = valid;
+    if (!FULL) {
+        const bool inwin = (px >= x.wx_lo) & (px < x.wx_hi) & (py >= x.wy_lo) & (py < x.wy_hi);
+        ok = valid & inwin;
+        fb = fb | (live & valid & !inwin);
+    }
+    px = ok ? px : x.zx;
+    py = ok ? py : x.zy;
+    m = ok ? m : 0.0f;
+    const float fx = floorf(px), fy = floorf(py);
+    const int x0 = (int)fx, y0 = (int)fy;
+    const float lx = px - fx, ly = py - fy;
+    const float hx = 1.0f - lx, hy = 1.0f - ly;
+    const float mhy = m * hy, mly = m * ly;
+    SlotCoef c;
+    c.w00 = mhy * hx;
+    c.w01 = mhy * lx;
+    c.w10 = mly * hx;
+    c.w11 = mly * lx;
+    c.a00 = __mul24(y0, x.row16) + __mul24(x0, x.xstep) + ubase;
+    return c;
+}
+
+// Lane v of every unit's lane group takes lane `src` of the same group.
+template <int SH, int SRC>
+__device__ __forceinline__ int unit_bcast(int val)
+{
+    constexpr int a = SH == 4 ? SRC : SRC, b = SH == 4 ? SRC : SRC, c = SH == 4 ? SRC : 2 + SRC,
+                  d = SH == 4 ? SRC : 2 + SRC;
+    return __builtin_amdgcn_mov_dpp(val, a | (b << 2) | (c << 4) | (d << 6), 0xF, 0xF, true);
+}
+
+// Point k's corners for this lane's vectors, its weights taken from the
+// lane that computed them.
+template <int NV, int SH, int K>
+__device__ __forceinline__ PointRegs<NV> issue_shared(const WinCtx& x, const SlotCoef* sc, int vbyte)
+{
+    constexpr int S = K / SH, SRC = K % SH;
+    PointRegs<NV> r;
+    r.w00 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w00)));
+    r.w01 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w01)));
+    r.w10 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w10)));
+    r.w11 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w11)));
+    const int a00 = unit_bcast<SH, SRC>(sc[S].a00) + vbyte;
+    const int a10 = a00 + x.row16;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const char* p0 = x.lbase + a00 + v * x.plane;
+        const char* p1 = x.lbase + a10 + v * x.plane;
+        r.v00[v] = *reinterpret_cast<const u32x4*>(p0);
+        r.v01[v] = *reinterpret_cast<const u32x4*>(p0 + x.xstep);
+        r.v10[v] = *reinterpret_cast<const u32x4*>(p1);
+        r.v11[v] = *reinterpret_cast<const u32x4*>(p1 + x.xstep);
+    }
+    return r;
+}
+
 // SPLIT (with NV = 1, no coalesced rows): a.lpu consecutive lanes share a
 // unit, lane v of them taking 16-byte vector v of the unit's channels (for
 // units of many vectors, whose whole-unit registers would cap a workgroup at
 // 512 threads).  The window then holds each pixel's vectors side by side,
 // (row, column, vector), so that a unit's lanes read neighbouring entries.
-template <int DT, int NV, int FULL, int RC, int COAL, int SPLIT, int MAXB>
+template <int DT, int NV, int FULL, int RC, int COAL, int SPLIT, int SHARE, int MAXB>
 __global__ void __launch_bounds__(MAXB)
 k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 {
+    static_assert(SHARE == 0 || (SPLIT && (SHARE == 2 || SHARE == 4)), "shared coefficients: split units");
     static_assert(!SPLIT || (NV == 1 && !COAL), "split units: one vector per lane, per-lane rows");
     using E = Elem<DT>;
     constexpr int s = E::kBytes;
@@ -545,18 +661,51 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         const int by = __mul24(oy, a.stride) - a.pad;
         const int ubase = SPLIT ? (int)((gl * a.nvt + vsub) * 16u) + cx.cbase : gl * NV * cx.plane + cx.cbase;
 
-        // two points in flight: issue the reads of point k+1, then accumulate point k
         bool fb = false;
-        PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, cm, 0, bx, by, ubase, fb);
+        if constexpr (SHARE) {
+            // this lane's points, then every point broadcast within the unit;
+            // two points in flight as below
+            constexpr int NS = (P + SHARE - 1) / SHARE;
+            const int v = (int)(lane & (SHARE - 1));
+            const int ucommon = ubase - (int)(vsub * 16u);   // the unit's vector 0
+            SlotCoef sc[NS];
+            static_for<NS>([&](auto sic) {
+                constexpr int si = decltype(sic)::value;
+                sc[si] = slot_coef<DT, FULL, RC, P, SHARE, si>(cx, co, cm, v, bx, by, ucommon, fb);
+            });
+            if (!FULL) {
+                // a unit is recomputed when any of its lanes found a point
+                // outside the window
+                int f = fb ? 1 : 0;
+                f |= __builtin_amdgcn_mov_dpp(f, 0xB1, 0xF, 0xF, true);            // quad_perm [1,0,3,2]
+                if (SHARE == 4) f |= __builtin_amdgcn_mov_dpp(f, 0x4E, 0xF, 0xF, true);   // [2,3,0,1]
+                fb = f != 0;
+            }
+            const int vbyte = (int)(vsub * 16u);
+            PointRegs<NV> cur = issue_shared<NV, SHARE, 0>(cx, sc, vbyte);
+            static_for<P>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                PointRegs<NV> nxt;
+                if constexpr (k + 1 < P) nxt = issue_shared<NV, SHARE, k + 1>(cx, sc, vbyte);
+                fence_sched();
+                pin(cur);
+                consume_point<DT, NV>(acc, cur);
+                fence_sched();
+                cur = nxt;
+            });
+        } else {
+            // two points in flight: issue the reads of point k+1, then accumulate point k
+            PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, cm, 0, bx, by, ubase, fb);
 #pragma unroll
-        for (int k = 0; k < P; ++k) {
-            PointRegs<NV> nxt;
-            if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, cm, k + 1, bx, by, ubase, fb);
-            fence_sched();
-            pin(cur);
-            consume_point<DT, NV>(acc, cur);
-            fence_sched();
-            cur = nxt;
+            for (int k = 0; k < P; ++k) {
+                PointRegs<NV> nxt;
+                if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, cm, k + 1, bx, by, ubase, fb);
+                fence_sched();
+                pin(cur);
+                consume_point<DT, NV>(acc, cur);
+                fence_sched();
+                cur = nxt;
+            }
         }
         // stored unconditionally (a unit marked in fbmask is recomputed and
         // stored again below): a store that depended on fb would let the
@@ -648,14 +797,14 @@ namespace {
 
 template <int NV> constexpr int kMaxBlock = NV <= 2 ? 1024 : 512;
 
-template <int DT, int NV, int FULL, int RC, int COAL, int SPLIT = 0>
+template <int DT, int NV, int FULL, int RC, int COAL, int SPLIT = 0, int SHARE = 0>
 hipError_t launch5(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
     if (block > kMaxBlock<NV> || block < 64 || block % 64) return hipErrorInvalidValue;
     const uint32_t total = (uint32_t)grid;
     const uint32_t per_xcd = (total + 7) / 8;
-    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, COAL, SPLIT, kMaxBlock<NV>>), dim3(per_xcd * 8), dim3(block),
-                       a.lds_bytes, stream, a, total, per_xcd);
+    hipLaunchKernelGGL((k_window<DT, NV, FULL, RC, COAL, SPLIT, SHARE, kMaxBlock<NV>>), dim3(per_xcd * 8),
+                       dim3(block), a.lds_bytes, stream, a, total, per_xcd);
     return hipGetLastError();
 }
 
@@ -666,16 +815,25 @@ hipError_t launch4(const KArgs& a, int block, int64_t grid, hipStream_t stream)
                   : launch5<DT, NV, FULL, RC, 0>(a, block, grid, stream);
 }
 
-// Units split over a.lpu lanes, one 16-byte vector each.
+// Units split over a.lpu lanes, one 16-byte vector each; units of 2 or 4
+// lanes share their points' coefficients (SH), others compute them per lane.
+template <int DT, int SH>
+hipError_t launch_split_sh(const KArgs& a, int block, int64_t grid, hipStream_t stream)
+{
+    if (a.full)
+        return a.remove_center ? launch5<DT, 1, 1, 1, 0, 1, SH>(a, block, grid, stream)
+                               : launch5<DT, 1, 1, 0, 0, 1, SH>(a, block, grid, stream);
+    return a.remove_center ? launch5<DT, 1, 0, 1, 0, 1, SH>(a, block, grid, stream)
+                           : launch5<DT, 1, 0, 0, 0, 1, SH>(a, block, grid, stream);
+}
+
 template <int DT>
 hipError_t launch_split(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
     if (a.coal || a.lpu < 2) return hipErrorInvalidValue;
-    if (a.full)
-        return a.remove_center ? launch5<DT, 1, 1, 1, 0, 1>(a, block, grid, stream)
-                               : launch5<DT, 1, 1, 0, 0, 1>(a, block, grid, stream);
-    return a.remove_center ? launch5<DT, 1, 0, 1, 0, 1>(a, block, grid, stream)
-                           : launch5<DT, 1, 0, 0, 0, 1>(a, block, grid, stream);
+    if (a.share && a.lpu == 4) return launch_split_sh<DT, 4>(a, block, grid, stream);
+    if (a.share && a.lpu == 2) return launch_split_sh<DT, 2>(a, block, grid, stream);
+    return launch_split_sh<DT, 0>(a, block, grid, stream);
 }
 
 template <int DT, int NV>

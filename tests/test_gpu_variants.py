@@ -120,3 +120,35 @@ def test_packed_offset_mask_rows(dtype, rc, Cg, tune, monkeypatch):
     dense = binding.forward(gu.dev(x, dtype), gu.dev(off, dtype), gu.dev(m, dtype), **gkw(wl))
     torch.cuda.synchronize()
     assert np.array_equal(gu.host(dense, dtype).view(np.uint8), want.view(np.uint8))
+
+
+# Units split over two or four lanes, with each point's coefficients computed
+# by one lane of the unit and broadcast to the others (share=1) or computed by
+# every lane (share=0): the same bits either way, on whole-image windows,
+# bands with the fallback, and 2-D tiles (split units of two 16-byte vectors
+# take tiles on wide images), with and without the centre point.
+SHARED = [
+    ("full_f32_4lanes", 2, 12, 13, 4, 16, 2.0, "f32", "kernel=window,split=1"),
+    ("bands_f32_4lanes", 2, 60, 60, 1, 16, 8.0, "f32", "kernel=window,full=0"),
+    ("bands_bf16_2lanes", 2, 60, 60, 2, 16, 6.0, "bf16", "kernel=window,full=0,split=1"),
+    ("tiles_bf16_2lanes", 1, 90, 200, 2, 16, 8.0, "bf16", "kernel=window,full=0,split=1,th=16,tw=64,r=12"),
+    ("full_f16_2lanes", 2, 14, 15, 2, 16, 3.0, "f16", "kernel=window,split=1"),
+]
+
+
+@pytest.mark.parametrize("rc", [False, True], ids=["all9", "rc"])
+@pytest.mark.parametrize("case", SHARED, ids=lambda c: c[0])
+def test_shared_point_coefficients_give_the_same_bits(case, rc, monkeypatch):
+    name, N, H, W, G, Cg, std, dt, tune = case
+    wl = Workload(name, N, H, W, G, Cg, (dt,), offset_dist=("normal", std), remove_center=rc, seed=71)
+    x, off, m = gen.make_inputs(wl, dt)
+    want = ref.forward_f32(x, off, m, dtype=dt, **okw(wl))
+    for share in ("0", "1"):
+        monkeypatch.setenv("DCNV4_TUNE", f"{tune},share={share}")
+        xd, od, md = gu.dev(x, dt), gu.dev(off, dt), gu.dev(m, dt)
+        plan = binding.query_plan(xd, od, md, torch.empty_like(xd), **gkw(wl))
+        assert plan["kernel"] == "window" and plan["lanes_per_unit"] in (2, 4), plan
+        gu.announce(f"shared coefficients {name} rc={rc} share={share} plan={plan}")
+        out = binding.forward(xd, od, md, **gkw(wl))
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.host(out, dt).view(np.uint8), want.view(np.uint8)), share
