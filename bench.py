@@ -351,17 +351,6 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def module_bytes(wl, dtype):
-    """The module's compulsory traffic: x_in read once and out written once
-    (C channels each), plus the weights (matrices in the I/O type, vectors in
-    binary32)."""
-    s = 4 if dtype == "f32" else 2
-    C, P, G = wl.C, wl.P, wl.G
-    R = 3 * G * P + G
-    px = wl.N * wl.H * wl.W
-    return 2 * px * C * s + (C * C + R * C + C * C) * s + (4 * C + 9 * C + R + C) * 4
-
-
 def bench_module(args, wl, dtype, log):
     """Time the module forward (group norm over min(32, C) groups, centre gate,
     output projection; Cin = Cout = C) on seeded random weights."""
@@ -370,6 +359,7 @@ def bench_module(args, wl, dtype, log):
 
     from deformable_convolution_vision_dcnv4_amd import binding
     from deformable_convolution_vision_dcnv4_amd import inputs as gen
+    from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
 
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]

@@ -31,7 +31,7 @@ import statistics
 import sys
 
 from . import build
-from .workloads import WORKLOADS
+from .workloads import WORKLOADS, module_bytes
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 OP_KERNEL_PREFIXES = ("void dcnv4::", "dcnv4::")
@@ -124,7 +124,7 @@ def main(argv=None):
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
-    ap.add_argument("--op", default="forward", choices=("forward", "backward"))
+    ap.add_argument("--op", default="forward", choices=("forward", "backward", "softmax", "module"))
     ap.add_argument("--command", required=True, help="the command line of the kernel-trace run")
     ap.add_argument("--counter-command", default=None,
                     help="the command line of the counter runs (COUNTER = FETCH_SIZE, then WRITE_SIZE)")
@@ -136,10 +136,16 @@ def main(argv=None):
     x_b = wl.N * wl.H * wl.W * wl.C * s
     off_b = wl.N * Ho * Wo * wl.G * 2 * wl.P * s
     m_b = wl.N * Ho * Wo * wl.G * wl.P * s
-    alg = wl.algorithmic_bytes(a.dtype) if a.op == "forward" else wl.backward_bytes(a.dtype)
-    what = (f"x {x_b} + offset {off_b} + mask {m_b} + out {x_b}" if a.op == "forward" else
-            f"x {x_b} + offset {off_b} + mask {m_b} + grad_out {x_b} read; binary32 gradients "
-            f"{x_b * 4 // s} + {off_b * 4 // s} + {m_b * 4 // s} written")
+    if a.op in ("forward", "softmax"):
+        alg = wl.algorithmic_bytes(a.dtype)
+        what = f"x {x_b} + offset {off_b} + mask {m_b} + out {x_b}"
+    elif a.op == "backward":
+        alg = wl.backward_bytes(a.dtype)
+        what = (f"x {x_b} + offset {off_b} + mask {m_b} + grad_out {x_b} read; binary32 gradients "
+                f"{x_b * 4 // s} + {off_b * 4 // s} + {m_b * 4 // s} written")
+    else:
+        alg = module_bytes(wl, a.dtype)
+        what = f"x_in {x_b} read + out {x_b} written + weights {alg - 2 * x_b}"
 
     def head(cmd):
         return [f"workload: {wl.describe(a.dtype)} ({a.op})",
@@ -153,16 +159,19 @@ def main(argv=None):
         for r in st:
             lines.append(f"{r['calls']:6d} {r['avg_us']:10.3f} {r['min_us']:10.3f} {r['max_us']:10.3f} "
                          f"{r['percent']:7.2f}  {r['name'][:110]}")
-        if a.op == "forward":
+        if a.op in ("forward", "softmax"):
             ops = [r for r in st if is_op(r["name"])]
-        else:
+        elif a.op == "backward":
             ops = [r for r in st if "k_backward" in r["name"] or "k_zero_f32" in r["name"]]
+        else:
+            ops = [r for r in st if r["name"].startswith(OP_KERNEL_PREFIXES)]
         for r in ops:
             lines.append("")
             lines.append(f"operator kernel: {r['name']}")
             lines.append(f"  mean duration {r['avg_us']:.3f} us")
         if ops:
-            launches = max(r["calls"] for r in ops)
+            # one launch of the operation = one call of its least-called kernel
+            launches = min(r["calls"] for r in ops)
             per_launch = sum(r["avg_us"] * r["calls"] for r in ops) / launches
             lines.append("")
             lines.append(f"per launch (all kernels of one {a.op}): {per_launch:.3f} us -> "

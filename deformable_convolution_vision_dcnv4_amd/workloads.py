@@ -99,6 +99,18 @@ WORKLOADS = {
 }
 
 
+def module_bytes(wl, dtype):
+    """The module forward's compulsory traffic on a workload's shape (C in,
+    C out, group norm, centre gate, output projection): x_in read once and
+    out written once, plus the weights (matrices in the I/O type, vectors and
+    depthwise taps in binary32)."""
+    s = 4 if dtype == "f32" else 2
+    C, P, G = wl.C, wl.P, wl.G
+    R = 3 * G * P + G
+    px = wl.N * wl.H * wl.W
+    return 2 * px * C * s + (C * C + R * C + C * C) * s + (4 * C + 9 * C + R + C) * 4
+
+
 # Every configuration the operator is measured and parity-tested on:
 # (workload, I/O type).  fiit_stage1 in f16 is the headline.
 CONFIGS = (("tiny", "f32"), ("fiit_stage1", "f32"), ("fiit_stage1", "f16"), ("fiit_stage3", "f16"),
