@@ -124,8 +124,13 @@ CASES = [
     (2, 9, 11, 24, 4, 8, 32, binding.NORM_NONE, 1, False, False, False, "f16"),
     (1, 13, 7, 20, 2, 12, 28, binding.NORM_LAYER, 1, True, True, True, "bf16"),
     (3, 5, 6, 7, 3, 5, 15, binding.NORM_GROUP, 3, False, True, False, "f32"),
-    # the FlashInternImage-T stage-1 shape (batch 2) and the latent shape (batch 1)
+    # binary32 rows of 256 and 640 bytes (the projection kernel's 4- and 10-vector forms)
+    (2, 6, 10, 64, 4, 16, 40, binding.NORM_GROUP, 8, False, True, True, "f32"),
+    (1, 5, 9, 160, 2, 8, 16, binding.NORM_NONE, 1, False, False, True, "f32"),
+    # the FlashInternImage-T stage-1 shape (batch 2, and batch 24: more row tiles
+    # than projection workgroups) and the latent shape (batch 1)
     (2, 56, 56, 64, 4, 16, 64, binding.NORM_GROUP, 32, False, True, True, "f16"),
+    (24, 56, 56, 64, 4, 16, 64, binding.NORM_GROUP, 32, False, True, True, "f16"),
     (1, 64, 64, 320, 8, 40, 320, binding.NORM_LAYER, 1, False, False, False, "bf16"),
 ]
 
