@@ -117,6 +117,8 @@ hipError_t launch_direct(const KArgs& a, int dtype, int block, int64_t grid, hip
 hipError_t launch_backward_om_window(const BArgs& a, int dtype, int nv, int block, size_t lds,
                                      hipStream_t stream);
 hipError_t launch_window(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);
+// The same launch with softmax-normalised weights (a.softmax, the DCNv3-style form).
+hipError_t launch_window_softmax(const KArgs& a, int dtype, int nv, int block, int64_t grid, hipStream_t stream);
 
 // Window kernel limits the planner needs: threads per workgroup it is
 // compiled for, and the LDS of the per-wave offset buffers of its

@@ -289,8 +289,7 @@ void plan_direct(const Problem& p, Plan* pl)
 void make_plan(const Problem& p, Plan* plan)
 {
     const Tune& t = tune();
-    // the softmax variant runs on the direct kernel only
-    if (t.kernel != 1 && !p.softmax && plan_window(p, plan)) return;
+    if (t.kernel != 1 && plan_window(p, plan)) return;
     plan_direct(p, plan);
 }
 
@@ -347,7 +346,8 @@ hipError_t launch_forward(const Problem& p, const Plan& plan, hipStream_t stream
     a.share = plan.share;
     a.nvt = plan.nv;
     a.div_lpu = make_fastdiv((uint32_t)plan.lpu);
-    return launch_window(a, p.dtype, plan.nv, plan.block, plan.grid, stream);
+    return p.softmax ? launch_window_softmax(a, p.dtype, plan.nv, plan.block, plan.grid, stream)
+                     : launch_window(a, p.dtype, plan.nv, plan.block, plan.grid, stream);
 }
 
 }  // namespace dcnv4

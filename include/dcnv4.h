@@ -122,7 +122,9 @@ int dcnv4_forward_ex(const void* x, const void* offset, const void* mask, void* 
  * in order of expf(m_k - mx); w_k = expf(m_k - mx) / S (IEEE division), then
  * the operation sequence above with w_k as the weight.  expf is the device
  * library's, so results match a reference to within its error, not bit for
- * bit.  Runs on the general (direct) kernel.
+ * bit.  Runs on the same kernels and plans as dcnv4_forward_ex; both kernel
+ * families compute the weights with the same binary32 operations and give
+ * the same bits.
  */
 int dcnv4_forward_softmax(const void* x, const void* offset, const void* mask, void* out,
                           int N, int H, int W, int G, int Cg,

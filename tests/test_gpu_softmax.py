@@ -1,5 +1,8 @@
 """GPU parity of the DCNv3-style aggregation (dcnv4_forward_softmax).
 
+Every case runs on both kernel families (the window family where the
+shape allows it, else the direct kernel again), which must agree bit for bit.
+
 Reference: the oracle's binary32 operation sequence fed with the oracle's
 softmax weights (double precision, rounded to binary32).  The GPU computes
 the weights in binary32 with the device's expf: each weight then differs
@@ -38,7 +41,7 @@ def ulp16(v, dtype):
     return 2.0 ** (e - mbits)
 
 
-def check(wl, dtype):
+def check(wl, dtype, monkeypatch):
     x, off, m = gen.make_inputs(wl, dtype)
     kw = dict(K=wl.K, stride=wl.stride, pad=wl.pad, dil=wl.dil, offset_scale=wl.offset_scale,
               remove_center=wl.remove_center)
@@ -51,15 +54,24 @@ def check(wl, dtype):
     tol = (2 * dm + P + 8) * U * A
     if dtype != "f32":
         tol = tol + ulp16(want, dtype)
-    gu.announce(f"softmax {wl.describe(dtype)} remove_center={wl.remove_center}")
-    out = binding.forward(gu.dev(x, dtype), gu.dev(off, dtype), gu.dev(m, dtype), kernel_size=wl.K,
-                          stride=wl.stride, pad=wl.pad, dilation=wl.dil, offset_scale=wl.offset_scale,
-                          remove_center=wl.remove_center, softmax=True)
-    torch.cuda.synchronize()
-    got = ref.to_f32(gu.host(out, dtype), dtype).astype(np.float64)
-    err = np.abs(got - want)
-    print(f"  max err {err.max():.3g}, max tol {tol.max():.3g}")
-    assert np.all(err <= tol), f"{np.sum(err > tol)} outputs beyond the bound"
+    xd, od, md = gu.dev(x, dtype), gu.dev(off, dtype), gu.dev(m, dtype)
+    outs = {}
+    # both kernel families (the window family where the shape allows it): the
+    # same weights and operation sequence, so the same bits
+    for fam in ("direct", "window"):
+        monkeypatch.setenv("DCNV4_TUNE", f"kernel={fam}")
+        gu.announce(f"softmax {wl.describe(dtype)} remove_center={wl.remove_center} kernel={fam}")
+        out = binding.forward(xd, od, md, kernel_size=wl.K, stride=wl.stride, pad=wl.pad, dilation=wl.dil,
+                              offset_scale=wl.offset_scale, remove_center=wl.remove_center, softmax=True)
+        torch.cuda.synchronize()
+        outs[fam] = gu.host(out, dtype)
+        got = ref.to_f32(outs[fam], dtype).astype(np.float64)
+        err = np.abs(got - want)
+        print(f"  {fam}: max err {err.max():.3g}, max tol {tol.max():.3g}")
+        assert np.all(err <= tol), f"{fam}: {np.sum(err > tol)} outputs beyond the bound"
+    monkeypatch.delenv("DCNV4_TUNE", raising=False)
+    assert np.array_equal(outs["direct"].view(np.uint8), outs["window"].view(np.uint8)), \
+        "the two kernel families disagree"
 
 
 CASES = [(Workload("sm", 2, 11, 13, 4, Cg, (dt,), offset_dist=("normal", 2.0), mask_dist=("normal", 2.0),
@@ -68,13 +80,17 @@ CASES = [(Workload("sm", 2, 11, 13, 4, Cg, (dt,), offset_dist=("normal", 2.0), m
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[1]}-Cg{c[0].Cg}{'-rc' if c[0].remove_center else ''}")
-def test_softmax_variant_matches_oracle(case):
-    check(*case)
+def test_softmax_variant_matches_oracle(case, monkeypatch):
+    check(*case, monkeypatch)
 
 
-@pytest.mark.parametrize("name,dtype", [("fiit_stage1", "f16"), ("fiit_stage3", "f16"), ("tiny", "f32")])
-def test_softmax_variant_workloads(name, dtype):
-    check(WORKLOADS[name], dtype)
+@pytest.mark.parametrize("name,dtype", [("fiit_stage1", "f16"), ("fiit_stage1", "f32"), ("fiit_stage3", "f16"),
+                                        ("hires", "bf16"), ("sd_latent", "bf16"), ("tiny", "f32")])
+def test_softmax_variant_workloads(name, dtype, monkeypatch):
+    """Every workload at full size: the whole-image window, bands of units
+    split over lanes with shared coefficients (stage-1 f32), tiles with the
+    global fallback (hires) and bands of five-vector units (latent)."""
+    check(WORKLOADS[name], dtype, monkeypatch)
 
 
 def test_softmax_of_huge_weights_is_finite_and_box_mean_for_equal_weights():
