@@ -41,15 +41,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 def load_counters(workload, dtype):
     """The committed rocprofv3 counter record of a workload (HBM bytes per
-    launch, L2 hits and misses), if it was taken on the current kernel
-    source; else None."""
+    launch, L2 hits and misses), if it was taken on the current source of the
+    forward operator's kernels; else None."""
     path = os.path.join(PROFILES, f"{workload}_{dtype}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     from deformable_convolution_vision_dcnv4_amd.build import source_hash
-    if rec.get("kernel_source_hash") != source_hash():
+    if rec.get("kernel_source_hash") != source_hash("forward"):
         return None
     return rec
 

@@ -29,14 +29,18 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def source_hash():
-    """Short digest of the kernel sources and the public header: names a
+def source_hash(scope="all"):
+    """Short digest of the kernel sources and the public headers: names a
     build, so that counter measurements can be matched to the code they
-    were taken on."""
+    were taken on.  scope="forward": only the files the forward operator's
+    kernels are built from (not the module's or the backward's), so that a
+    change elsewhere keeps the forward's counter records valid."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(CSRC, "*"))) + sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
     for path in files:
         if not os.path.isfile(path) or path.endswith((".so", ".tmp")):
+            continue
+        if scope == "forward" and any(w in os.path.basename(path) for w in ("module", "backward")):
             continue
         with open(path, "rb") as fh:
             h.update(os.path.basename(path).encode() + b"\0" + fh.read())

@@ -150,7 +150,7 @@ def main(argv=None):
     def head(cmd):
         return [f"workload: {wl.describe(a.dtype)} ({a.op})",
                 f"algorithmic bytes per launch: {alg} ({what})",
-                f"kernel source hash: {build.source_hash()}",
+                f"kernel source hash: {build.source_hash()} (forward kernels: {build.source_hash('forward')})",
                 f"command: {cmd}", ""]
 
     if a.stats:
@@ -187,7 +187,8 @@ def main(argv=None):
         fetch_b = f_kib * 1024.0 * f_fac
         write_b = w_kib * 1024.0 * w_fac
         ccmd = a.counter_command or a.command
-        rec = {"workload": a.workload, "dtype": a.dtype, "kernel_source_hash": build.source_hash(),
+        rec = {"workload": a.workload, "dtype": a.dtype,
+               "kernel_source_hash": build.source_hash("forward" if a.op == "forward" else "all"),
                "command": ccmd,
                "fetch_kib_per_dispatch": round(f_kib, 3), "fetch_factor": round(f_fac, 4),
                "write_kib_per_dispatch": round(w_kib, 3), "write_factor": round(w_fac, 4),

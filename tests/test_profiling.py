@@ -64,7 +64,7 @@ def test_summary_scales_counters_by_copy_calibration(tmp_path):
     assert abs(rec["hbm_read_bytes_per_launch"] - 1.1 * (x_b + off_b + m_b)) <= 2
     assert abs(rec["hbm_write_bytes_per_launch"] - x_b) <= 2
     assert rec["algorithmic_bytes_per_launch"] == wl.algorithmic_bytes("f16")
-    assert rec["kernel_source_hash"] == build.source_hash()
+    assert rec["kernel_source_hash"] == build.source_hash("forward")
     assert rec["command"] == "CCMD"
     txt = open(out + "_kernel_trace.txt").read()
     assert "command: CMD" in txt and "50.000" in txt
@@ -117,3 +117,5 @@ def test_summary_reports_l2_hit_rate_and_per_unit_counts(tmp_path):
 def test_source_hash_is_stable_and_short():
     h = build.source_hash()
     assert h == build.source_hash() and len(h) == 16
+    f = build.source_hash("forward")
+    assert f == build.source_hash("forward") and len(f) == 16 and f != h
