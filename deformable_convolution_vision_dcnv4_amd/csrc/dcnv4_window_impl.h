@@ -740,23 +740,35 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
                 cur = nxt;
             }
         }
-        // stored unconditionally (a unit marked in fbmask is recomputed and
-        // stored again below): a store that depended on fb would let the
-        // compiler sink every multiply-add of the unit below the branch and
-        // keep all nine points' corner data alive at once
         if (!FULL) fbmask |= (uint64_t)fb << pass;
 
-        char* op;
-        if (COAL) {
-            op = static_cast<char*>(a.out) + (int64_t)n * a.img_out_elems * s + oo;
-        } else {
-            const int64_t pix = (int64_t)oy * a.Wo + ox;
-            op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s +
-                 vsub * 16u;
-        }
+        if (FULL) {
+            char* op;
+            if (COAL) {
+                op = static_cast<char*>(a.out) + (int64_t)n * a.img_out_elems * s + oo;
+            } else {
+                const int64_t pix = (int64_t)oy * a.Wo + ox;
+                op = static_cast<char*>(a.out) + ((int64_t)n * a.img_out_elems + pix * a.C + (int64_t)g * a.Cg) * s +
+                     vsub * 16u;
+            }
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-            *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
+            for (int v = 0; v < NV; ++v)
+                *reinterpret_cast<u32x4*>(op + 16 * v) = pack_vec16<DT>(acc + v * EPV);
+        } else {
+            // a unit marked in fbmask is recomputed and stored below, so its
+            // store here goes to an offset out of the buffer's range, which the
+            // hardware drops.  No branch: a store that depended on fb would let
+            // the compiler sink every multiply-add of the unit below the branch
+            // and keep all nine points' corner data alive at once
+            const __amdgpu_buffer_rsrc_t rout =
+                make_rsrc(static_cast<char*>(a.out) + (int64_t)n * a.img_out_elems * s, (uint32_t)(a.img_out_elems * s));
+            const uint32_t at = COAL ? oo
+                                     : (uint32_t)((((int64_t)oy * a.Wo + ox) * a.C + (int64_t)g * a.Cg) * s) + vsub * 16u;
+            const uint32_t o = fb ? kOobOffset : at;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                __builtin_amdgcn_raw_buffer_store_b128(pack_vec16<DT>(acc + v * EPV), rout, (int)(o + 16u * v), 0, 0);
+        }
     };
     uint32_t pass = 0;
     if (COAL) {
