@@ -216,129 +216,6 @@ __global__ void __launch_bounds__(256) k_gemm(const void* __restrict__ a, int64_
     }
 }
 
-// Vector form of k_gemm for 16-byte aligned operands with K * s a multiple
-// of 16 and at most KV * 64 bytes.  A workgroup of 8 waves loads the weights
-// of its column range [n0, n0 + NB) for all of K into LDS once (zero past K
-// and past the last column) and then walks row tiles of 128 rows (16 per
-// wave) with a grid stride, requesting the next tile's rows before the
-// current tile's products.  Lane (i, kg) = (lane % 16, lane / 16) reads row
-// i's elements [(4v + kg) E, (4v + kg + 1) E) as its 16-byte vector v
-// (E = 16 / s) and feeds them to E / kPer MFMA steps, kPer at a time; the
-// weight fragment of the same lane and step is the same k range of column j
-// from LDS.  Every step thus pairs each k with itself: a permutation of the
-// contraction's products over the steps, accumulated in binary32.  The
-// results go through a per-wave LDS tile to 16-byte row-wise stores.
-// Grid: passes * GR workgroups, workgroup b taking pass b % passes.
-constexpr int kGemmvWaves = 8;
-constexpr int kGemmvMaxBlocks = 10;   // column blocks of 16 per pass (NB <= 160)
-
-// One wave's 16 rows of tile t (128 rows per tile) as KV 16-byte vectors per
-// lane, vector v of lane (li, kg) holding row li's bytes [(4v + kg) 16, + 16);
-// zeros past M, past K and for t >= T.
-template <int DT, int KV>
-__device__ __forceinline__ void gemmv_rows(const void* a, int64_t lda, int64_t M, int K, int64_t t, int64_t T,
-                                           uint32_t wave, int li, int kg, u32x4 (&fa)[KV])
-{
-    constexpr int s = Elem<DT>::kBytes;
-    const int64_t r0 = t * 128 + wave * 16;
-    const int rows_here = (t < T && r0 < M) ? (int)min<int64_t>(16, M - r0) : 0;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const char*>(a) + (rows_here ? r0 : 0) * lda * s,
-                                                rows_here ? (uint32_t)(((int64_t)(rows_here - 1) * lda + K) * s) : 0u);
-    const int kbytes = K * s;
-#pragma unroll
-    for (int v = 0; v < KV; ++v) {
-        const int kb = (4 * v + kg) * 16;
-        const bool in = (li < rows_here) & (kb < kbytes);
-        fa[v] = buf_load16(ra, in ? (uint32_t)((int64_t)li * lda * s + kb) : kOobOffset);
-    }
-}
-
-template <int DT, int KV>
-__global__ void __launch_bounds__(512) k_gemmv(const void* __restrict__ a, int64_t lda, const void* __restrict__ w,
-                                               const float* __restrict__ bias, void* __restrict__ out, int64_t ldo,
-                                               int64_t M, int K, int Nn, int NB, int passes, int wpitch)
-{
-    using MF = Mfma<DT>;
-    using E = Elem<DT>;
-    using S = typename E::S;
-    constexpr int s = E::kBytes, EV = 16 / s, STEPS = EV / MF::kPer;
-    extern __shared__ __align__(16) unsigned char lds[];
-    const int pass = blockIdx.x % passes, GR = gridDim.x / passes, rg0 = blockIdx.x / passes;
-    const int n0 = pass * NB, nbb = NB / 16;
-    const int opitch = NB * s + 16;                        // bytes per row of the output tile
-    unsigned char* wt = lds;                               // [NB][wpitch bytes]
-    unsigned char* ot = lds + NB * wpitch + (threadIdx.x >> 6) * 16 * opitch;
-    // weights: column n0 + r, bytes [0, KV * 64) of its k range, zero past K and Nn
-    const int kbytes = K * s, vrow = KV * 4;                // 16-byte vectors per staged column
-    for (int e = threadIdx.x; e < NB * vrow; e += blockDim.x) {
-        const int r = e / vrow, c = e - r * vrow;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (n0 + r < Nn && c * 16 < kbytes)
-            v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(w) + (int64_t)(n0 + r) * kbytes + c * 16);
-        *reinterpret_cast<u32x4*>(wt + r * wpitch + c * 16) = v;
-    }
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const int li = (int)(lane & 15u), kg = (int)(lane >> 4);
-    float bn[kGemmvMaxBlocks];
-#pragma unroll
-    for (int b = 0; b < kGemmvMaxBlocks; ++b) {
-        const int col = n0 + 16 * b + li;
-        bn[b] = (b < nbb && col < Nn) ? bias[col] : 0.f;
-    }
-    __syncthreads();
-    const int64_t T = (M + 127) / 128;
-    u32x4 fa[KV], fn[KV];
-    int64_t t = rg0;
-    gemmv_rows<DT, KV>(a, lda, M, K, t, T, wave, li, kg, fa);
-    for (; t < T; t += GR) {
-        gemmv_rows<DT, KV>(a, lda, M, K, t + GR, T, wave, li, kg, fn);
-        f4 acc[kGemmvMaxBlocks];
-#pragma unroll
-        for (int b = 0; b < kGemmvMaxBlocks; ++b) acc[b] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < KV; ++v) {
-#pragma unroll
-            for (int b = 0; b < kGemmvMaxBlocks; ++b) {
-                if (b >= nbb) continue;   // (uniform)
-                const u32x4 wv = *reinterpret_cast<const u32x4*>(wt + (16 * b + li) * wpitch + (4 * v + kg) * 16);
-#pragma unroll
-                for (int e = 0; e < STEPS; ++e) acc[b] = MF::mma(MF::part(fa[v], e), MF::part(wv, e), acc[b]);
-            }
-        }
-        // bias, one rounding, to the wave's tile: row 4 * kg + r, column 16 * b + li
-#pragma unroll
-        for (int b = 0; b < kGemmvMaxBlocks; ++b) {
-            if (b >= nbb) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<S*>(ot + (4 * kg + r) * opitch + (16 * b + li) * s) = E::from_f(acc[b][r] + bn[b]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int64_t r0 = t * 128 + wave * 16;
-        const int cpr = NB / EV;                            // 16-byte chunks per tile row
-        for (int c = (int)lane; c < 16 * cpr; c += 64) {
-            const int r = c / cpr, q = c - r * cpr;
-            const int col = n0 + q * EV;
-            if (r0 + r >= M || col >= Nn) continue;
-            const unsigned char* src = ot + r * opitch + q * 16;
-            char* dst = static_cast<char*>(out) + ((r0 + r) * ldo + col) * s;
-            if (col + EV <= Nn) {
-                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-            } else {
-                for (int e = 0; e < Nn - col; ++e)
-                    reinterpret_cast<S*>(dst)[e] = reinterpret_cast<const S*>(src)[e];
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int v = 0; v < KV; ++v) fa[v] = fn[v];
-    }
-}
-
 // Thread index -> (pixel, channel chunk) for the elementwise kernels, with
 // unsigned 32-bit divisions when the grid's threads number below 2^31 (the
 // common case; 64-bit division is a long instruction sequence).
@@ -391,6 +268,187 @@ __device__ __forceinline__ void store_vals(void* p, const float* v)
         *static_cast<typename E::S*>(p) = E::from_f(v[0]);
     } else {
         *static_cast<u32x4*>(p) = pack_vec16<DT>(v);
+    }
+}
+
+// Vector form of k_gemm for 16-byte aligned operands with K * s a multiple
+// of 16 and at most KV * 64 bytes.  A workgroup of 8 waves loads the weights
+// of its column range [n0, n0 + NB) for all of K into LDS once (zero past K
+// and past the last column) and then walks row tiles of 128 rows (16 per
+// wave) with a grid stride, requesting the next tile's rows before the
+// current tile's products.  Lane (i, kg) = (lane % 16, lane / 16) reads row
+// i's elements [(4v + kg) E, (4v + kg + 1) E) as its 16-byte vector v
+// (E = 16 / s) and feeds them to E / kPer MFMA steps, kPer at a time; the
+// weight fragment of the same lane and step is the same k range of column j
+// from LDS.  Every step thus pairs each k with itself: a permutation of the
+// contraction's products over the steps, accumulated in binary32.  The
+// results go through a per-wave LDS tile to 16-byte row-wise stores.
+// Grid: passes * GR workgroups, workgroup b taking pass b % passes.
+constexpr int kGemmvWaves = 8;
+constexpr int kGemmvMaxBlocks = 10;   // column blocks of 16 per pass (NB <= 160)
+
+// The centre-feature gate applied while the output projection reads its
+// rows (GATE): the projection's input row is gated = round(y * (1 - s) +
+// xn * s), s = sigmoid(rows[pix][gate0 + c / Cg]), the same operations as
+// k_gate, so the same values; y is the kernel's `a`, xn has the same layout.
+struct GateSrc {
+    const void* xn;
+    const void* rows;
+    int64_t rstride;   // elements per pixel of rows
+    int gate0, Cg;
+};
+
+// One wave's 16 rows of tile t (128 rows per tile) as KV 16-byte vectors per
+// lane, vector v of lane (li, kg) holding row li's bytes [(4v + kg) 16, + 16);
+// zeros past M, past K and for t >= T.  GATE: also xn's vectors and the raw
+// gate logit of each vector's group (a vector lies in one group).
+template <int DT, int KV, int GATE>
+__device__ __forceinline__ void gemmv_rows(const void* a, int64_t lda, int64_t M, int K, int64_t t, int64_t T,
+                                           uint32_t wave, int li, int kg, const GateSrc& gs, u32x4 (&fa)[KV],
+                                           u32x4 (&fx)[KV], uint32_t (&fl)[KV])
+{
+    constexpr int s = Elem<DT>::kBytes;
+    const int64_t r0 = t * 128 + wave * 16;
+    const int rows_here = (t < T && r0 < M) ? (int)min<int64_t>(16, M - r0) : 0;
+    const uint32_t span = rows_here ? (uint32_t)(((int64_t)(rows_here - 1) * lda + K) * s) : 0u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const char*>(a) + (rows_here ? r0 : 0) * lda * s, span);
+    const int kbytes = K * s;
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+        const int kb = (4 * v + kg) * 16;
+        const bool in = (li < rows_here) & (kb < kbytes);
+        fa[v] = buf_load16(ra, in ? (uint32_t)((int64_t)li * lda * s + kb) : kOobOffset);
+    }
+    if constexpr (GATE) {
+        const __amdgpu_buffer_rsrc_t rx =
+            make_rsrc(static_cast<const char*>(gs.xn) + (rows_here ? r0 : 0) * lda * s, span);
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(
+            static_cast<const char*>(gs.rows) + (rows_here ? r0 : 0) * gs.rstride * s,
+            rows_here ? (uint32_t)((int64_t)rows_here * gs.rstride * s) : 0u);
+#pragma unroll
+        for (int v = 0; v < KV; ++v) {
+            const int kb = (4 * v + kg) * 16;
+            const bool in = (li < rows_here) & (kb < kbytes);
+            fx[v] = buf_load16(rx, in ? (uint32_t)((int64_t)li * lda * s + kb) : kOobOffset);
+            const int g = kb / s / gs.Cg;
+            const uint32_t lo = in ? (uint32_t)(((int64_t)li * gs.rstride + gs.gate0 + g) * s) : kOobOffset;
+            if constexpr (s == 4)
+                fl[v] = __builtin_amdgcn_raw_buffer_load_b32(rr, (int)lo, 0, 0);
+            else
+                fl[v] = __builtin_amdgcn_raw_buffer_load_b16(rr, (int)lo, 0, 0);
+        }
+    }
+}
+
+// y's vector gated with xn's, one rounding per element (as k_gate).
+template <int DT>
+__device__ __forceinline__ u32x4 gate_vector(u32x4 y, u32x4 x, uint32_t logit_raw)
+{
+    constexpr int EV = kPerVec<DT>;
+    const float tl = Elem<DT>::raw_to_f(logit_raw);
+    const float sg = 1.0f / (1.0f + expf(-tl));
+    float yv[EV], xv[EV];
+    load_vals<DT, EV>(&y, yv);
+    load_vals<DT, EV>(&x, xv);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) yv[e] = yv[e] * (1.0f - sg) + xv[e] * sg;
+    return pack_vec16<DT>(yv);
+}
+
+template <int DT, int KV, int GATE>
+__global__ void __launch_bounds__(512) k_gemmv(const void* __restrict__ a, int64_t lda, const void* __restrict__ w,
+                                               const float* __restrict__ bias, void* __restrict__ out, int64_t ldo,
+                                               int64_t M, int K, int Nn, int NB, int passes, int wpitch, GateSrc gs)
+{
+    using MF = Mfma<DT>;
+    using E = Elem<DT>;
+    using S = typename E::S;
+    constexpr int s = E::kBytes, EV = 16 / s, STEPS = EV / MF::kPer;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int pass = blockIdx.x % passes, GR = gridDim.x / passes, rg0 = blockIdx.x / passes;
+    const int n0 = pass * NB, nbb = NB / 16;
+    const int opitch = NB * s + 16;                        // bytes per row of the output tile
+    unsigned char* wt = lds;                               // [NB][wpitch bytes]
+    unsigned char* ot = lds + NB * wpitch + (threadIdx.x >> 6) * 16 * opitch;
+    // weights: column n0 + r, bytes [0, KV * 64) of its k range, zero past K and Nn
+    const int kbytes = K * s, vrow = KV * 4;                // 16-byte vectors per staged column
+    for (int e = threadIdx.x; e < NB * vrow; e += blockDim.x) {
+        const int r = e / vrow, c = e - r * vrow;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (n0 + r < Nn && c * 16 < kbytes)
+            v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(w) + (int64_t)(n0 + r) * kbytes + c * 16);
+        *reinterpret_cast<u32x4*>(wt + r * wpitch + c * 16) = v;
+    }
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const int li = (int)(lane & 15u), kg = (int)(lane >> 4);
+    float bn[kGemmvMaxBlocks];
+#pragma unroll
+    for (int b = 0; b < kGemmvMaxBlocks; ++b) {
+        const int col = n0 + 16 * b + li;
+        bn[b] = (b < nbb && col < Nn) ? bias[col] : 0.f;
+    }
+    __syncthreads();
+    const int64_t T = (M + 127) / 128;
+    u32x4 fa[KV], fn[KV], xa[KV], xn_[KV];
+    uint32_t la[KV], ln[KV];
+    int64_t t = rg0;
+    gemmv_rows<DT, KV, GATE>(a, lda, M, K, t, T, wave, li, kg, gs, fa, xa, la);
+    for (; t < T; t += GR) {
+        gemmv_rows<DT, KV, GATE>(a, lda, M, K, t + GR, T, wave, li, kg, gs, fn, xn_, ln);
+        if constexpr (GATE) {
+#pragma unroll
+            for (int v = 0; v < KV; ++v) fa[v] = gate_vector<DT>(fa[v], xa[v], la[v]);
+        }
+        f4 acc[kGemmvMaxBlocks];
+#pragma unroll
+        for (int b = 0; b < kGemmvMaxBlocks; ++b) acc[b] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < KV; ++v) {
+#pragma unroll
+            for (int b = 0; b < kGemmvMaxBlocks; ++b) {
+                if (b >= nbb) continue;   // (uniform)
+                const u32x4 wv = *reinterpret_cast<const u32x4*>(wt + (16 * b + li) * wpitch + (4 * v + kg) * 16);
+#pragma unroll
+                for (int e = 0; e < STEPS; ++e) acc[b] = MF::mma(MF::part(fa[v], e), MF::part(wv, e), acc[b]);
+            }
+        }
+        // bias, one rounding, to the wave's tile: row 4 * kg + r, column 16 * b + li
+#pragma unroll
+        for (int b = 0; b < kGemmvMaxBlocks; ++b) {
+            if (b >= nbb) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<S*>(ot + (4 * kg + r) * opitch + (16 * b + li) * s) = E::from_f(acc[b][r] + bn[b]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t r0 = t * 128 + wave * 16;
+        const int cpr = NB / EV;                            // 16-byte chunks per tile row
+        for (int c = (int)lane; c < 16 * cpr; c += 64) {
+            const int r = c / cpr, q = c - r * cpr;
+            const int col = n0 + q * EV;
+            if (r0 + r >= M || col >= Nn) continue;
+            const unsigned char* src = ot + r * opitch + q * 16;
+            char* dst = static_cast<char*>(out) + ((r0 + r) * ldo + col) * s;
+            if (col + EV <= Nn) {
+                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+            } else {
+                for (int e = 0; e < Nn - col; ++e)
+                    reinterpret_cast<S*>(dst)[e] = reinterpret_cast<const S*>(src)[e];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int v = 0; v < KV; ++v) {
+            fa[v] = fn[v];
+            if constexpr (GATE) {
+                xa[v] = xn_[v];
+                la[v] = ln[v];
+            }
+        }
     }
 }
 
@@ -792,13 +850,33 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // kernel when the operands allow it (16-byte aligned rows and pointers,
 // K * s a multiple of 16 and at most 640 bytes), else k_gemm.
 template <int DT>
-void gemm(const void* a, int64_t lda, const void* w, const float* bias, void* out, int64_t ldo, int64_t M, int K,
-          int Nn, int cus, hipStream_t st)
+bool gemm_vector_ok(const void* a, int64_t lda, const void* w, const void* out, int64_t ldo, int K)
 {
     constexpr int s = Elem<DT>::kBytes;
     const int64_t kb = (int64_t)K * s;
-    const bool vec = kb % 16 == 0 && kb <= 640 && (lda * s) % 16 == 0 && (ldo * s) % 16 == 0 &&
-                     (uintptr_t)a % 16 == 0 && (uintptr_t)w % 16 == 0 && (uintptr_t)out % 16 == 0;
+    return kb % 16 == 0 && kb <= 640 && (lda * s) % 16 == 0 && (ldo * s) % 16 == 0 && (uintptr_t)a % 16 == 0 &&
+           (uintptr_t)w % 16 == 0 && (uintptr_t)out % 16 == 0;
+}
+
+// The gate can ride on the projection: vector kernel, rows of at most 256
+// bytes (wider ones need more registers than the gated form has), and each
+// 16-byte vector within one group.
+template <int DT>
+bool gemm_gate_ok(const void* a, int64_t lda, const void* w, const void* out, int64_t ldo, int K, int Cg)
+{
+    return gemm_vector_ok<DT>(a, lda, w, out, ldo, K) && (int64_t)K * Elem<DT>::kBytes <= 256 &&
+           Cg % kPerVec<DT> == 0;
+}
+
+// gate (optional): apply the centre-feature gate to the rows as they are
+// read (the caller checks gemm_gate_ok).
+template <int DT>
+void gemm(const void* a, int64_t lda, const void* w, const float* bias, void* out, int64_t ldo, int64_t M, int K,
+          int Nn, int cus, hipStream_t st, const GateSrc* gate = nullptr)
+{
+    constexpr int s = Elem<DT>::kBytes;
+    const int64_t kb = (int64_t)K * s;
+    const bool vec = gemm_vector_ok<DT>(a, lda, w, out, ldo, K);
     if (!vec || M == 0) {
         if (M > 0)
             hipLaunchKernelGGL(k_gemm<DT>, dim3((unsigned)cdiv(M, 64)), dim3(256), 0, st, a, lda, w, bias, out, ldo,
@@ -818,15 +896,18 @@ void gemm(const void* a, int64_t lda, const void* w, const float* bias, void* ou
     const int per_cu = kv == 10 ? 1 : 2;
     const int64_t gr = std::max<int64_t>(1, std::min<int64_t>(T, (int64_t)cus * per_cu / passes));
     const dim3 grid((unsigned)(gr * passes)), block(64 * kGemmvWaves);
-    if (kv == 2)
-        hipLaunchKernelGGL((k_gemmv<DT, 2>), grid, block, lds, st, a, lda, w, bias, out, ldo, M, K, Nn, NB, passes,
-                           wpitch);
-    else if (kv == 4)
-        hipLaunchKernelGGL((k_gemmv<DT, 4>), grid, block, lds, st, a, lda, w, bias, out, ldo, M, K, Nn, NB, passes,
-                           wpitch);
-    else
-        hipLaunchKernelGGL((k_gemmv<DT, 10>), grid, block, lds, st, a, lda, w, bias, out, ldo, M, K, Nn, NB, passes,
-                           wpitch);
+    const GateSrc gs = gate ? *gate : GateSrc{nullptr, nullptr, 0, 0, 1};
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, block, lds, st, a, lda, w, bias, out, ldo, M, K, Nn, NB, passes, wpitch, gs);
+    };
+    if (gate) {
+        if (kv == 2) go(k_gemmv<DT, 2, 1>);
+        else go(k_gemmv<DT, 4, 1>);   // (kv <= 4: gemm_gate_ok)
+    } else {
+        if (kv == 2) go(k_gemmv<DT, 2, 0>);
+        else if (kv == 4) go(k_gemmv<DT, 4, 0>);
+        else go(k_gemmv<DT, 10, 0>);
+    }
 }
 
 template <int DT>
@@ -925,8 +1006,17 @@ hipError_t run(const ModuleProblem& m, hipStream_t st)
         e = launch_forward(p, plan, st);
         if (e != hipSuccess) return e;
     }
-    // 6. centre-feature gate, 7. output projection
+    // 6. centre-feature gate, 7. output projection: the gate is applied by the
+    // projection as it reads its rows when the vector kernel takes it (each
+    // 16-byte vector within one group), else by k_gate into the workspace
     void* last = y;
+    const bool fuse = m.center_scale && m.out_proj &&
+                      gemm_gate_ok<DT>(y, (int64_t)C, m.w.w_out, m.out, (int64_t)m.Cout, C, m.Cg);
+    if (fuse) {
+        const GateSrc gs{xn, rows, L.rows_stride, 3 * m.G * L.P, m.Cg};
+        gemm<DT>(y, (int64_t)C, m.w.w_out, m.w.b_out, m.out, (int64_t)m.Cout, npix, C, m.Cout, m.cus, st, &gs);
+        return hipGetLastError();
+    }
     if (m.center_scale) {
         void* g = L.gated >= 0 ? ws + L.gated : m.out;
         if (vec)

@@ -34,6 +34,11 @@
  *             y = y * (1 - s) + xn * s   (the pixel's own normalised feature)
  *   7. out  = y @ w_out^T + b_out (optional output projection, Cout channels),
  *             else out = y (Cout = C)
+ * With both 6 and 7, the gate is applied while the projection reads its
+ * rows -- the same operations and rounding, the gated rows not stored --
+ * when C * s <= 256 bytes, Cg * s is a multiple of 16 and out and w_out are
+ * 16-byte aligned (s = bytes per element); otherwise the gated rows go to
+ * the workspace first.
  * Each step's result is rounded once to the I/O type (nearest even) and read
  * back as such by the next step; arithmetic inside a step is binary32 (the
  * normalisation statistics binary64).  Step 5 is the operator of dcnv4.h,
@@ -91,7 +96,9 @@ typedef struct dcnv4_module_weights {
 
 /* Byte offsets of the intermediates in the workspace (each 256-byte
  * aligned); a region a configuration does not use has offset -1.  Row
- * strides in elements: C for xp, xn, d, y and gated; rows_stride for rows. */
+ * strides in elements: C for xp, xn, d, y and gated; rows_stride for rows.
+ * gated (gate and output projection both on) is written only when the
+ * projection does not apply the gate itself (step 6 above). */
 typedef struct dcnv4_module_layout {
     int64_t xp, xn, d, rows, y, gated;  /* [N,H,W,.] in the I/O type */
     int64_t stats;                      /* group-norm statistics (binary64 partial sums, then

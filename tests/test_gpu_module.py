@@ -178,19 +178,63 @@ def test_module_forward_step_by_step(case):
                              remove_center=rc, groups=G)
     y_h = region(ws, lay, "y", shape, dtype) if (cs or op) else gu.host(out, dtype)
     assert np.array_equal(y_h.view(np.uint8), y_want.view(np.uint8)), "operator step differs from the oracle"
-    last_h = y_h
-    # 6. centre-feature gate
+    # 6. centre-feature gate, 7. output projection
+    gate_and_projection(ws, lay, gu.host(out, dtype), y_h, xn, rows, w64, G, P, cs, op, dtype, stored=False)
+
+
+def gate_and_projection(ws, lay, out_h, y_h, xn, rows, w64, G, P, cs, op, dtype, stored):
+    """Steps 6 and 7 against the oracle applied to the stored y and xn.  With
+    both steps the library may apply the gate while the projection reads its
+    rows (nothing stored in between): the output is then checked against the
+    oracle's gate and projection, the gate's error (its bound, plus half an
+    ulp of the I/O type for the rounding of each gated value) carried through
+    the projection's weights.  stored: the gated rows are in the workspace
+    (the gate ran as its own kernel) and are checked as a step of their own."""
+    f = lambda a: gen.as_f64(a, dtype)  # noqa: E731
+    shape = y_h.shape
+    C = shape[-1]
+    yv = f(y_h)
+    last = yv
     if cs:
-        g_h = region(ws, lay, "gated", shape, dtype) if op else gu.host(out, dtype)
-        yv = f(y_h)
-        want = om.centre_scale(yv, xn, rows[..., 3 * G * P:3 * G * P + G], G)
-        check("centre gate", f(g_h), want, 8 * U * (np.abs(yv) + np.abs(xn)) + U * np.abs(want), dtype)
-        last_h = g_h
-    # 7. output projection
+        g_ref = om.centre_scale(yv, xn, rows[..., 3 * G * P:3 * G * P + G], G)
+        g_bound = 8 * U * (np.abs(yv) + np.abs(xn)) + U * np.abs(g_ref)
+        if not op or stored:
+            g_h = region(ws, lay, "gated", shape, dtype) if op else out_h
+            check("centre gate", f(g_h), g_ref, g_bound, dtype)
+            last = f(g_h)
+        else:
+            eg = g_bound + (0.5 * ulp(np.abs(g_ref) + g_bound, dtype) if dtype != "f32" else 0.0)
+            want = om.conv1x1(g_ref, w64["w_out"], w64["b_out"])
+            bound = (om.conv1x1(eg, np.abs(w64["w_out"]), np.zeros_like(w64["b_out"])) +
+                     (C + 2) * U * om.abs_terms_conv1x1(np.abs(g_ref) + eg, w64["w_out"], w64["b_out"]))
+            check("centre gate and output projection", f(out_h), want, bound, dtype)
+            return
     if op:
-        lv = f(last_h)
-        check("output projection", f(gu.host(out, dtype)), om.conv1x1(lv, w64["w_out"], w64["b_out"]),
-              (C + 2) * U * om.abs_terms_conv1x1(lv, w64["w_out"], w64["b_out"]), dtype)
+        check("output projection", f(out_h), om.conv1x1(last, w64["w_out"], w64["b_out"]),
+              (C + 2) * U * om.abs_terms_conv1x1(last, w64["w_out"], w64["b_out"]), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_module_gate_in_its_own_kernel_when_the_output_is_unaligned(dtype):
+    """An output that is not 16-byte aligned keeps the gate in its own kernel
+    (the vector projection needs aligned rows): the gated rows are then in
+    the workspace and checked as a step, and the projection on them."""
+    N, H, W, Cin, G, Cg, Cout = 2, 9, 11, 24, 4, 16, 32
+    C = G * Cg
+    x_h, x64, dev, w64, cfg, P, R = make_module(13, N, H, W, Cin, G, Cg, Cout, binding.NORM_GROUP, 8, False, True,
+                                                True, dtype)
+    n = N * H * W * Cout
+    big = torch.empty(n + 8, dtype=TDT[dtype], device="cuda")
+    out = big[1:1 + n].view(N, H, W, Cout)
+    assert out.data_ptr() % 16 != 0
+    out, ws, lay = binding.module_forward(gu.dev(x_h, dtype), dev, cfg, out=out)
+    torch.cuda.synchronize()
+    shape = (N, H, W, C)
+    f = lambda a: gen.as_f64(a, dtype)  # noqa: E731
+    xn = f(region(ws, lay, "xn", shape, dtype))
+    rows = f(region(ws, lay, "rows", (N, H, W, R), dtype, stride=lay["rows_stride"]))[..., :R]
+    y_h = region(ws, lay, "y", shape, dtype)
+    gate_and_projection(ws, lay, gu.host(out, dtype), y_h, xn, rows, w64, G, P, True, True, dtype, stored=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
