@@ -21,7 +21,10 @@ bytes per launch measured by rocprofv3 counters on the same kernel source
 = the L2 hit rate from the same counter runs (TCC_HIT / (TCC_HIT + TCC_MISS)).
 `configs` = every other measured configuration (the five workloads' I/O
 types), event-timed in the same run the same way, with each one's fraction
-of sampling points outside the image.  `cpu_baseline` = the CPU oracle on
+of sampling points outside the image; then the backward, the DCNv3-style
+variant and the module forward on the named workload (algorithmic bytes:
+the backward's inputs read and binary32 gradients written; the module's
+input read, output written and weights).  `cpu_baseline` = the CPU oracle on
 one thread and on all the cores the process may use (one thread per slice of
 images; the oracle itself stays single-threaded code).
 """
@@ -285,7 +288,8 @@ def main():
             ccnt = load_counters(name, cdt)
             oob, corner = oob_fractions(cwl, gen.as_f64(cr["inputs"][1], cdt))
             configs.append({
-                "workload": cwl.describe(cdt), "dtype": cdt, "kernel_us_mean": round(cr["kern_ms"] * 1e3, 3),
+                "workload": cwl.describe(cdt), "dtype": cdt, "op": "forward",
+                "kernel_us_mean": round(cr["kern_ms"] * 1e3, 3),
                 "gbs": round(cbytes / (cr["kern_ms"] * 1e-3) / 1e9, 2),
                 "hbm_fraction": round(cbytes / (cr["kern_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gsamples_per_s": round(cwl.samples() / (cr["kern_ms"] * 1e-3) / 1e9, 3),
@@ -295,6 +299,24 @@ def main():
                 "points_outside": round(oob, 4), "points_with_a_corner_outside": round(corner, 4),
                 "l2_hit": ccnt.get("l2_hit") if ccnt else None,
                 "hbm_traffic": ccnt.get("hbm_bytes_per_launch") if ccnt else None,
+            })
+        # the other operations on this workload: backward, the DCNv3-style
+        # variant and the whole module forward, event-timed the same way
+        from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
+        for cop in ("backward", "softmax", "module"):
+            if cop == "module":
+                cr = time_module(wl, dtype, args.config_steps, max(5, args.warmup // 4), log)
+                cbytes = module_bytes(wl, dtype)
+            else:
+                cr = measure(wl, dtype, cop, args.config_steps, max(5, args.warmup // 4), args.rotate_bytes,
+                             per_launch=False)
+                cbytes = wl.backward_bytes(dtype) if cop == "backward" else wl.algorithmic_bytes(dtype)
+            configs.append({
+                "workload": wl.describe(dtype), "dtype": dtype, "op": cop,
+                "kernel_us_mean": round(cr["kern_ms"] * 1e3, 3),
+                "gbs": round(cbytes / (cr["kern_ms"] * 1e-3) / 1e9, 2),
+                "hbm_fraction": round(cbytes / (cr["kern_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": cbytes, "steps": args.config_steps,
             })
 
     cpu = None
@@ -351,15 +373,15 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def bench_module(args, wl, dtype, log):
+def time_module(wl, dtype, steps, warmup, log):
     """Time the module forward (group norm over min(32, C) groups, centre gate,
-    output projection; Cin = Cout = C) on seeded random weights."""
+    output projection; Cin = Cout = C) on seeded random weights: the wall
+    time and the event time of `steps` back-to-back forwards."""
     import numpy as np
     import torch
 
     from deformable_convolution_vision_dcnv4_amd import binding
     from deformable_convolution_vision_dcnv4_amd import inputs as gen
-    from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
 
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
@@ -392,31 +414,41 @@ def bench_module(args, wl, dtype, log):
     lay = binding.module_layout(wl.N, wl.H, wl.W, cfg, tdt)
     ws = torch.empty(lay["total"], dtype=torch.uint8, device=dev)
     out = torch.empty((wl.N, wl.H, wl.W, C), dtype=tdt, device=dev)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         binding.module_forward(xs, weights, cfg, out=out, workspace=ws)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         binding.module_forward(xs, weights, cfg, out=out, workspace=ws)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = ev0.elapsed_time(ev1) / steps
+    log(f"timed {steps} module forwards: {ms * 1e3:.2f} us each (events), workspace {lay['total'] / 2**20:.1f} MiB")
+    return {"wall_s": wall, "kern_ms": ms, "workspace_bytes": lay["total"], "norm_groups": min(32, C)}
+
+
+def bench_module(args, wl, dtype, log):
+    """The module forward's JSON line (--op module)."""
+    from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
+
+    r = time_module(wl, dtype, args.steps, args.warmup, log)
+    ms = r["kern_ms"]
     alg = module_bytes(wl, dtype)
-    log(f"timed {args.steps} module forwards: {ms * 1e3:.2f} us each (events), workspace {lay['total'] / 2**20:.1f} MiB")
-    ms_step = wall * 1e3 / args.steps
+    ms_step = r["wall_s"] * 1e3 / args.steps
+    C = wl.C
     rec = {
         "metric": "DCNv4 module fwd GB/s per MI355X (x in + out + weights); % of HBM roofline",
         "value": round(alg / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded inputs and random weights; no dataset, no trained weights)",
-        "config": {"workload": wl.describe(dtype), "op": "module", "norm": "group", "norm_groups": min(32, C),
+        "config": {"workload": wl.describe(dtype), "op": "module", "norm": "group", "norm_groups": r["norm_groups"],
                    "center_scale": True, "out_proj": True, "Cin": C, "Cout": C,
-                   "algorithmic_bytes_per_step": alg, "workspace_bytes": lay["total"]},
+                   "algorithmic_bytes_per_step": alg, "workspace_bytes": r["workspace_bytes"]},
         "kernel_us_mean": round(ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
