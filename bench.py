@@ -9,6 +9,13 @@ launch reading HBM rather than the 256 MB Infinity Cache, the timed loop
 rotates over several copies of the inputs (at least 1 GiB in all), so a copy
 is reused only after >= 1 GiB of other traffic.
 
+Before the W warmup launches, --spinup-s seconds (default 1) of the same
+launches run untimed: the GPU leaves its idle clocks and every rotating copy
+is touched, so that the K timed launches measure the steady state (measured
+on the stage-1 f16 shape: 43-44 us per launch after 20 warmup launches
+alone, 39 us after about a second of launches).  The JSON records the
+spin-up.
+
 Printed: one JSON line.  `value` = algorithmic bytes per step / wall-clock
 time per step over the timed region.  `roofline.achieved` = the same bytes /
 the kernel's mean launch duration, taken from two HIP events recorded on the
@@ -132,6 +139,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="time the named workload only")
     ap.add_argument("--config-steps", type=int, default=50, help="timed launches per other configuration")
+    ap.add_argument("--spinup-s", type=float, default=1.0,
+                    help="seconds of the workload's own launches before the warmup steps, so that the timed "
+                         "launches run at the GPU's steady clocks with every rotating copy touched (0: none)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -163,9 +173,24 @@ def main():
     torch.cuda.set_device(dev)
     binding.lib()
 
-    def measure(wl, dtype, op, steps, warmup, rotate_gib, per_launch=True):
+    def spin_up(step, seconds):
+        """Launch `step` back to back for about `seconds` (untimed): the GPU
+        leaves its idle clocks and every rotating copy's pages are touched."""
+        if seconds <= 0:
+            return 0
+        n, t0 = 0, time.perf_counter()
+        while True:
+            for _ in range(64):
+                step(n)
+                n += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
+
+    def measure(wl, dtype, op, steps, warmup, rotate_gib, per_launch=True, spinup_s=0.0):
         """Time `steps` back-to-back launches of `op` on wl's synthetic inputs
-        (resident in HBM, rotating over >= rotate_gib GiB of copies)."""
+        (resident in HBM, rotating over >= rotate_gib GiB of copies), after
+        spinup_s seconds of untimed launches and `warmup` warmup launches."""
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
         dcode = {"f32": binding.F32, "f16": binding.F16, "bf16": binding.BF16}[dtype]
         log(f"workload {wl.describe(dtype)}; generating inputs (seed {wl.seed})")
@@ -226,6 +251,9 @@ def main():
                                   stride=wl.stride, pad=wl.pad, dilation=wl.dil, offset_scale=wl.offset_scale)
         log(f"plan {plan}")
 
+        nspin = spin_up(step, spinup_s)
+        if nspin:
+            log(f"spin-up: {nspin} launches in about {spinup_s:.2f} s")
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -245,7 +273,8 @@ def main():
         kern_ms = region_ms / steps
         log(f"timed {steps} steps: wall {wall * 1e3:.3f} ms, events {region_ms:.3f} ms, "
             f"{kern_ms * 1e3:.2f} us per launch")
-        r = {"wall_s": wall, "kern_ms": kern_ms, "copies": copies, "plan": plan, "inputs": (x, off, m)}
+        r = {"wall_s": wall, "kern_ms": kern_ms, "copies": copies, "plan": plan, "inputs": (x, off, m),
+             "spinup_launches": nspin}
         if per_launch:
             # secondary: one event pair per launch (adds the events' own cost; for a
             # short kernel it also shows host-side launch latency)
@@ -266,7 +295,7 @@ def main():
 
     if args.op == "module":
         return bench_module(args, wl, dtype, log)
-    r = measure(wl, dtype, args.op, args.steps, args.warmup, args.rotate_bytes)
+    r = measure(wl, dtype, args.op, args.steps, args.warmup, args.rotate_bytes, spinup_s=args.spinup_s)
     x, off, m = r["inputs"]
     alg_bytes = wl.backward_bytes(dtype) if args.op == "backward" else wl.algorithmic_bytes(dtype)
     ms_per_step = r["wall_s"] * 1e3 / args.steps
@@ -283,7 +312,7 @@ def main():
                 continue
             cwl = WORKLOADS[name]
             cr = measure(cwl, cdt, "forward", args.config_steps, max(5, args.warmup // 4), args.rotate_bytes,
-                         per_launch=False)
+                         per_launch=False, spinup_s=min(args.spinup_s, 0.3))
             cbytes = cwl.algorithmic_bytes(cdt)
             ccnt = load_counters(name, cdt)
             oob, corner = oob_fractions(cwl, gen.as_f64(cr["inputs"][1], cdt))
@@ -305,11 +334,12 @@ def main():
         from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
         for cop in ("backward", "softmax", "module"):
             if cop == "module":
-                cr = time_module(wl, dtype, args.config_steps, max(5, args.warmup // 4), log)
+                cr = time_module(wl, dtype, args.config_steps, max(5, args.warmup // 4), log,
+                                 spinup_s=min(args.spinup_s, 0.3))
                 cbytes = module_bytes(wl, dtype)
             else:
                 cr = measure(wl, dtype, cop, args.config_steps, max(5, args.warmup // 4), args.rotate_bytes,
-                             per_launch=False)
+                             per_launch=False, spinup_s=min(args.spinup_s, 0.3))
                 cbytes = wl.backward_bytes(dtype) if cop == "backward" else wl.algorithmic_bytes(dtype)
             configs.append({
                 "workload": wl.describe(dtype), "dtype": dtype, "op": cop,
@@ -350,6 +380,7 @@ def main():
             "algorithmic_bytes_per_step": alg_bytes,
             "samples_per_step": wl.samples(),
             "rotating_copies": r["copies"],
+            "spinup": {"seconds": args.spinup_s, "launches": r["spinup_launches"]},
             "plan": r["plan"],
             "points_outside": round(oob, 4),
             "points_with_a_corner_outside": round(corner, 4),
@@ -373,7 +404,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def time_module(wl, dtype, steps, warmup, log):
+def time_module(wl, dtype, steps, warmup, log, spinup_s=0.0):
     """Time the module forward (group norm over min(32, C) groups, centre gate,
     output projection; Cin = Cout = C) on seeded random weights: the wall
     time and the event time of `steps` back-to-back forwards."""
@@ -414,6 +445,11 @@ def time_module(wl, dtype, steps, warmup, log):
     lay = binding.module_layout(wl.N, wl.H, wl.W, cfg, tdt)
     ws = torch.empty(lay["total"], dtype=torch.uint8, device=dev)
     out = torch.empty((wl.N, wl.H, wl.W, C), dtype=tdt, device=dev)
+    t_spin = time.perf_counter()
+    while spinup_s > 0 and time.perf_counter() - t_spin < spinup_s:
+        for _ in range(16):
+            binding.module_forward(xs, weights, cfg, out=out, workspace=ws)
+        torch.cuda.synchronize()
     for _ in range(warmup):
         binding.module_forward(xs, weights, cfg, out=out, workspace=ws)
     torch.cuda.synchronize()
@@ -435,7 +471,7 @@ def bench_module(args, wl, dtype, log):
     """The module forward's JSON line (--op module)."""
     from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
 
-    r = time_module(wl, dtype, args.steps, args.warmup, log)
+    r = time_module(wl, dtype, args.steps, args.warmup, log, spinup_s=args.spinup_s)
     ms = r["kern_ms"]
     alg = module_bytes(wl, dtype)
     ms_step = r["wall_s"] * 1e3 / args.steps
