@@ -147,7 +147,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the operator is measured on one GPU's share "
-              "(multi-GPU sharding is not part of this build); use --gpus 1", file=sys.stderr)
+              "(running it sharded over several GPUs is not implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
