@@ -366,6 +366,7 @@ int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const 
     plan->full_window = pl.full;
     plan->lds_bytes = pl.lds_total;
     plan->coalesced_offsets = pl.coal;
+    plan->shared_coefficients = pl.kernel == dcnv4::kKernelWindow ? pl.share : 0;
     return DCNV4_OK;
 }
 

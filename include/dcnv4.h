@@ -209,6 +209,10 @@ typedef struct dcnv4_plan {
     int lds_bytes;        /* LDS per workgroup (window and offset-row buffers) */
     int coalesced_offsets; /* window family: 1 if each wave stages its units' offset rows
                               through LDS with in-order loads */
+    int shared_coefficients; /* window family, units split over lanes: 1 if each lane computes
+                                a share of the points' positions and weights and the unit's
+                                lanes exchange them (quad permutation), 0 if every lane
+                                computes all of them */
 } dcnv4_plan;
 
 int dcnv4_query_plan(const void* x, const void* offset, const void* mask, const void* out,

@@ -150,6 +150,23 @@ def test_plan_tuning_variable_is_read_again_when_it_changes(monkeypatch):
     assert st == OK and pl.as_dict()["kernel"] == "window" and pl.full_window == 1
 
 
+@pytest.mark.parametrize("dtype,Cg,N,H,W,G,tune,lanes,shared", [
+    (0, 16, 64, 56, 56, 4, None, 4, 1),        # stage-1 fp32: four lanes share the coefficients
+    (0, 16, 64, 56, 56, 4, "share=0", 4, 0),
+    (1, 16, 64, 56, 56, 4, None, 1, 0),        # stage-1 fp16: whole units per lane
+    (2, 16, 2, 256, 256, 8, None, 2, 0),       # 256x256 bf16: two lanes, sharing only on request
+    (2, 16, 2, 256, 256, 8, "share=1", 2, 1),
+    (2, 40, 8, 64, 64, 8, None, 5, 0)])        # latent: five lanes, no quad to share in
+def test_plan_reports_shared_coefficients(dtype, Cg, N, H, W, G, tune, lanes, shared, monkeypatch):
+    if tune:
+        monkeypatch.setenv("DCNV4_TUNE", tune)
+    else:
+        monkeypatch.delenv("DCNV4_TUNE", raising=False)
+    st, pl = plan(dtype=dtype, Cg=Cg, N=N, H=H, W=W, G=G)
+    assert st == OK and pl.as_dict()["kernel"] == "window"
+    assert pl.lanes_per_unit == lanes and pl.shared_coefficients == shared
+
+
 def test_plan_full_window_for_small_images():
     # 8x8 image, 4 groups of 16 fp16 channels: the whole zero-bordered image fits
     st, pl = plan(dtype=1, Cg=16, N=64, H=14, W=14, G=16)
