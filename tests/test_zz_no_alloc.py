@@ -62,3 +62,38 @@ def test_noalloc_module_rejects_problems_beyond_its_scratch():
     st = binding.lib().dcnv4_module_forward_noalloc(0x10000000, ctypes.byref(w), 0x20000000, 64, 56, 56,
                                                    ctypes.byref(cfg), 1, None)
     assert st == 6 and "no-allocation" in binding.last_error()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_noalloc_module_captured_in_a_graph_replays_the_eager_result(dtype):
+    """The callers it is for: code under HIP graph capture.  The entry point
+    is captured once (its scratch address was looked up by an eager call
+    before), then the graph is replayed several times with new input values
+    copied in between and eager work and synchronisations around the
+    replays; every replay must equal the workspace entry point's eager
+    result on the same input, bit for bit."""
+    N, H, W, Cin, G, Cg, Cout = 2, 12, 14, 32, 4, 8, 24
+    x_h, _, dev, _, cfg, _, _ = make_module(23, N, H, W, Cin, G, Cg, Cout, binding.NORM_GROUP, 8, False, True,
+                                           True, dtype)
+    x = gu.dev(x_h, dtype)
+    out = torch.empty((N, H, W, Cout), dtype=x.dtype, device=x.device)
+    assert _noalloc(x, dev, cfg, out) == 0, binding.last_error()   # eager call first
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = _noalloc(x, dev, cfg, out)
+    assert st == 0, binding.last_error()
+    torch.cuda.synchronize()
+    gen_ = torch.Generator(device="cpu").manual_seed(5)
+    for i in range(4):
+        # new input values in the captured buffer, eager work around the replay
+        x.copy_((torch.randn(x.shape, generator=gen_) * (1 + i)).to(x.dtype))
+        want, _, _ = binding.module_forward(x, dev, cfg)
+        torch.cuda.synchronize()
+        gu.announce(f"graph replay {i} {dtype}")
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = gu.host(out, dtype), gu.host(want, dtype)
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {i} differs from the eager result"
