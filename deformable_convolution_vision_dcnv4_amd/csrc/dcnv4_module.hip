@@ -7,20 +7,24 @@
 // feature scaling through a sigmoid: pwwt.cn/news/2159231 section "进阶优化建议".
 //
 // Kernels (each step's result rounded once to the I/O type):
-//   k_gemm       rows @ W^T + b on the matrix cores: one wave per 16 rows,
-//                MFMA 16x16x16 (f16, bf16) or 16x16x4 (f32) with binary32
-//                accumulation, 8 column blocks of 16 per pass so that a row
-//                fragment is loaded once per pass.  The projections and the
-//                predictor are dense contractions over the channels, the one
-//                part of the module that is.
+//   k_gemmv      rows @ W^T + b on the matrix cores (MFMA 16x16x16 f16/bf16,
+//                16x16x4 f32, binary32 accumulation) for 16-byte aligned rows
+//                of at most 640 bytes: the weights held in LDS across a
+//                grid-stride walk over row tiles; optionally applies the
+//                centre-feature gate to its rows as they are read.  k_gemm:
+//                the general form.  The projections and the predictor are
+//                dense contractions over the channels, the one part of the
+//                module that is.
 //   k_gn_partial / k_gn_finalize
 //                group-norm statistics: binary64 sums per (image, slice of
 //                pixels, channel), then per (image, group) in a fixed order
 //                (reproducible), mean and 1/sqrt(var + eps).
 //   k_norm       applies the group norm (or computes and applies a layer norm,
 //                one wave per pixel, binary64 sums) -> xn.
-//   k_dw3x3      depthwise 3x3, zero padding -> d.
-//   k_gate       centre-feature gate y * (1 - s) + xn * s.
+//   k_dw3x3v     depthwise 3x3, zero padding -> d, runs of four pixels per
+//                thread with the taps in LDS; k_dw3x3: the general form.
+//   k_gate       centre-feature gate y * (1 - s) + xn * s, when the output
+//                projection does not apply it.
 // The operator in between is the dcnv4_forward_ex kernel family on xn and the
 // predictor's rows, read in place with the rows' stride.
 
