@@ -143,9 +143,16 @@ def _id(c):
 
 @pytest.mark.parametrize("case", CASES, ids=_id)
 def test_module_forward_step_by_step(case):
+    check_case(case)
+
+
+def check_case(case, seed=7, offset_std=1.5):
+    """Run one module configuration through the C ABI and check every step
+    against the module oracle applied to the GPU's previous step."""
     N, H, W, Cin, G, Cg, Cout, norm, ng, rc, cs, op, dtype = case
     C = G * Cg
-    x_h, x64, dev, w64, cfg, P, R = make_module(7, N, H, W, Cin, G, Cg, Cout, norm, ng, rc, cs, op, dtype)
+    x_h, x64, dev, w64, cfg, P, R = make_module(seed, N, H, W, Cin, G, Cg, Cout, norm, ng, rc, cs, op, dtype,
+                                                offset_std=offset_std)
     gu.announce(f"module {_id(case)}")
     out, ws, lay = binding.module_forward(gu.dev(x_h, dtype), dev, cfg)
     torch.cuda.synchronize()
