@@ -247,8 +247,8 @@ bool plan_window(const Problem& p, Plan* pl)
     pl->lanes = lpu;
     pl->lpu = lpu;
     // point coefficients shared over a unit's lanes: four lanes (stage-1 fp32:
-    // 70.9-78.9 us against 75.6-79.7 without); two lanes measured slower
-    // (the 256x256 bf16 shape: 136.7 against 123.6 us), so only on request
+    // 67.1 us against 74.0 without); two lanes measured slower (the 256x256
+    // bf16 shape: 126.2 against 122.2 us), so only on request
     pl->share = (lpu == 4 && t.share != 0) || (lpu == 2 && t.share == 1) ? 1 : 0;
     pl->block = block;
     pl->nv = nv;
