@@ -248,8 +248,10 @@ bool plan_window(const Problem& p, Plan* pl)
     pl->lpu = lpu;
     // point coefficients shared over a unit's lanes: four lanes (stage-1 fp32:
     // 67.1 us against 74.0 without); two lanes measured slower (the 256x256
-    // bf16 shape: 126.2 against 122.2 us), so only on request
-    pl->share = (lpu == 4 && t.share != 0) || (lpu == 2 && t.share == 1) ? 1 : 0;
+    // bf16 shape: 126.2 against 122.2 us), so only on request; one group per
+    // workgroup (the kernel's corner reads step over a pixel's vectors with a
+    // constant offset)
+    pl->share = GB == 1 && ((lpu == 4 && t.share != 0) || (lpu == 2 && t.share == 1)) ? 1 : 0;
     pl->block = block;
     pl->nv = nv;
     pl->GB = GB; pl->TH = TH; pl->TW = TW; pl->RY = full ? 0 : R; pl->RX = full ? 0 : R;

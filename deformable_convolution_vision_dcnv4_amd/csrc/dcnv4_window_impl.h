@@ -192,7 +192,7 @@ struct WinCtx {
 template <int DT, int NV, int FULL, int RC, int P, int SPLIT, typename MR>
 __device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
                                                      const MR& msk, int k, int bx, int by,
-                                                     int ubase, bool& fb)
+                                                     const char* ub, bool& fb)
 {
     PointRegs<NV> r;
     const int q = (RC && k >= 4) ? k + 1 : k;
@@ -222,13 +222,15 @@ __device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowL
     r.w01 = mhy * lx;
     r.w10 = mly * hx;
     r.w11 = mly * lx;
-    const int a00 = __mul24(y0, x.row16) + (SPLIT ? __mul24(x0, x.xstep) : (x0 << 4)) + ubase;
-    const int a10 = a00 + x.row16;
+    // ub: the unit's vector 0 at window pixel (0, 0) of this LDS (its base
+    // added once per unit, not once per point)
+    const char* p00 = ub + (__mul24(y0, x.row16) + (SPLIT ? __mul24(x0, x.xstep) : (x0 << 4)));
+    const char* p10 = p00 + x.row16;
     const int step01 = SPLIT ? x.xstep : 16;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        const char* p0 = x.lbase + a00 + v * x.plane;
-        const char* p1 = x.lbase + a10 + v * x.plane;
+        const char* p0 = p00 + v * x.plane;
+        const char* p1 = p10 + v * x.plane;
         r.v00[v] = *reinterpret_cast<const u32x4*>(p0);
         r.v01[v] = *reinterpret_cast<const u32x4*>(p0 + step01);
         r.v10[v] = *reinterpret_cast<const u32x4*>(p1);
@@ -393,26 +395,27 @@ __device__ __forceinline__ int unit_bcast(int val)
 
 // Point k's corners for this lane's vectors, its weights taken from the
 // lane that computed them.
+// Shared coefficients need one group per workgroup, so a window pixel holds
+// the unit's SH vectors and horizontally adjacent pixels are 16*SH bytes
+// apart (an immediate offset of the corner reads).  vb: this lane's vector
+// at LDS byte 0.
 template <int NV, int SH, int K>
-__device__ __forceinline__ PointRegs<NV> issue_shared(const WinCtx& x, const SlotCoef* sc, int vbyte)
+__device__ __forceinline__ PointRegs<NV> issue_shared(const WinCtx& x, const SlotCoef* sc, const char* vb)
 {
+    static_assert(NV == 1, "shared coefficients: one vector per lane");
     constexpr int S = K / SH, SRC = K % SH;
+    constexpr int XS = 16 * SH;
     PointRegs<NV> r;
     r.w00 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w00)));
     r.w01 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w01)));
     r.w10 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w10)));
     r.w11 = __int_as_float(unit_bcast<SH, SRC>(__float_as_int(sc[S].w11)));
-    const int a00 = unit_bcast<SH, SRC>(sc[S].a00) + vbyte;
-    const int a10 = a00 + x.row16;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const char* p0 = x.lbase + a00 + v * x.plane;
-        const char* p1 = x.lbase + a10 + v * x.plane;
-        r.v00[v] = *reinterpret_cast<const u32x4*>(p0);
-        r.v01[v] = *reinterpret_cast<const u32x4*>(p0 + x.xstep);
-        r.v10[v] = *reinterpret_cast<const u32x4*>(p1);
-        r.v11[v] = *reinterpret_cast<const u32x4*>(p1 + x.xstep);
-    }
+    const char* p0 = vb + unit_bcast<SH, SRC>(sc[S].a00);
+    const char* p1 = p0 + x.row16;
+    r.v00[0] = *reinterpret_cast<const u32x4*>(p0);
+    r.v01[0] = *reinterpret_cast<const u32x4*>(p0 + XS);
+    r.v10[0] = *reinterpret_cast<const u32x4*>(p1);
+    r.v11[0] = *reinterpret_cast<const u32x4*>(p1 + XS);
     return r;
 }
 
@@ -546,9 +549,15 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         for (uint32_t c0 = threadIdx.x; c0 < nchunks || !rows_issued; c0 += B * U) {
             u32x4 v[U];
             uint32_t dst[U];
+            // the wave's first chunk of this round (lane 0's), the same in every lane
+            const uint32_t wc0 = __builtin_amdgcn_readfirstlane(c0 - lane);
 #pragma unroll
             for (int r = 0; r < U; ++r) {
                 const uint32_t c = c0 + r * B;
+                // no chunk of the wave left in this slot: its address arithmetic
+                // and load are skipped (a small window leaves most slots empty);
+                // the LDS write below tests each lane's own chunk
+                if (wc0 + r * B >= nchunks) continue;
                 const uint32_t p = fdiv(c, a.div_CPS);
                 const uint32_t cc = c - p * CPS;
                 const uint32_t wyl = fdiv(p, a.div_pitch);
@@ -714,12 +723,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
                 if (SHARE == 4) f |= __builtin_amdgcn_mov_dpp(f, 0x4E, 0xF, 0xF, true);   // [2,3,0,1]
                 fb = f != 0;
             }
-            const int vbyte = (int)(vsub * 16u);
-            PointRegs<NV> cur = issue_shared<NV, SHARE, 0>(cx, sc, vbyte);
+            const char* vb = cx.lbase + vsub * 16u;
+            PointRegs<NV> cur = issue_shared<NV, SHARE, 0>(cx, sc, vb);
             static_for<P>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
                 PointRegs<NV> nxt;
-                if constexpr (k + 1 < P) nxt = issue_shared<NV, SHARE, k + 1>(cx, sc, vbyte);
+                if constexpr (k + 1 < P) nxt = issue_shared<NV, SHARE, k + 1>(cx, sc, vb);
                 fence_sched();
                 pin(cur);
                 consume_point<DT, NV>(acc, cur);
@@ -728,11 +737,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             });
         } else {
             // two points in flight: issue the reads of point k+1, then accumulate point k
-            PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, 0, bx, by, ubase, fb);
+            const char* ub = cx.lbase + ubase;
+            PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, 0, bx, by, ub, fb);
 #pragma unroll
             for (int k = 0; k < P; ++k) {
                 PointRegs<NV> nxt;
-                if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, k + 1, bx, by, ubase, fb);
+                if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, k + 1, bx, by, ub, fb);
                 fence_sched();
                 pin(cur);
                 consume_point<DT, NV>(acc, cur);
@@ -873,6 +883,9 @@ template <int SM, int DT>
 hipError_t launch_split(const KArgs& a, int block, int64_t grid, hipStream_t stream)
 {
     if (a.coal || a.lpu < 2) return hipErrorInvalidValue;
+    // shared coefficients address a window pixel's lpu vectors with a constant
+    // step: one group per workgroup, as many vectors as lanes
+    if (a.share && (a.GB != 1 || a.nvt != a.lpu)) return hipErrorInvalidValue;
     if (a.share && a.lpu == 4) return launch_split_sh<SM, DT, 4>(a, block, grid, stream);
     if (a.share && a.lpu == 2) return launch_split_sh<SM, DT, 2>(a, block, grid, stream);
     return launch_split_sh<SM, DT, 0>(a, block, grid, stream);

@@ -156,7 +156,8 @@ def test_plan_tuning_variable_is_read_again_when_it_changes(monkeypatch):
     (1, 16, 64, 56, 56, 4, None, 1, 0),        # stage-1 fp16: whole units per lane
     (2, 16, 2, 256, 256, 8, None, 2, 0),       # 256x256 bf16: two lanes, sharing only on request
     (2, 16, 2, 256, 256, 8, "share=1", 2, 1),
-    (2, 40, 8, 64, 64, 8, None, 5, 0)])        # latent: five lanes, no quad to share in
+    (2, 40, 8, 64, 64, 8, None, 5, 0),         # latent: five lanes, no quad to share in
+    (0, 16, 64, 56, 56, 4, "gb=2", 4, 0)])     # two groups per workgroup: no sharing
 def test_plan_reports_shared_coefficients(dtype, Cg, N, H, W, G, tune, lanes, shared, monkeypatch):
     if tune:
         monkeypatch.setenv("DCNV4_TUNE", tune)
