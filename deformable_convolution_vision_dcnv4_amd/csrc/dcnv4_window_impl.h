@@ -345,21 +345,51 @@ __device__ __forceinline__ float row_pick(const Row& r, int base, int v)
     return x;
 }
 
+// This lane's points' offsets and weights only (lane v of a unit computes
+// points v, v + SH, ...; a slot past the unit's points reads point P - 1),
+// one element load each, so that no lane holds the unit's whole rows or
+// selects from them.  Same prefetch protocol as RowLoad: issue one unit
+// ahead, read after the wait.
+template <int DT, int P, int SH>
+struct SlotRows {
+    static constexpr int NS = (P + SH - 1) / SH;
+    static constexpr uint32_t kEl = Elem<DT>::kBytes;
+    uint32_t ox[NS], oy[NS], m[NS];
+
+    static __device__ __forceinline__ uint32_t load_el(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    {
+        if constexpr (kEl == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    }
+    // so / sm: byte offsets of the unit's offset and weight rows; v: this
+    // lane's place in its unit
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, uint32_t so,
+                                          uint32_t sm, int v)
+    {
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const uint32_t k = (uint32_t)min(t * SH + v, P - 1);
+            ox[t] = load_el(ro, so + k * kEl);
+            oy[t] = load_el(ro, so + ((uint32_t)P + k) * kEl);
+            m[t] = load_el(rm, sm + k * kEl);
+        }
+    }
+};
+
 // Slot s of this lane (point k = s * SH + v): the steps of issue_point up to
-// the corner address; `live` is false for a k past the unit's points.
-template <int DT, int FULL, int RC, int P, int SH, int S, typename MR>
-__device__ __forceinline__ SlotCoef slot_coef(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
-                                              const MR& msk, int v, int bx, int by, int ubase,
-                                              bool& fb)
+// the corner address, from the point's x and y offsets and weight; `live` is
+// false for a k past the unit's points.
+template <int FULL, int RC, int P, int SH, int S>
+__device__ __forceinline__ SlotCoef slot_coef_of(const WinCtx& x, float ox, float oy, float m, int v, int bx,
+                                                 int by, int ubase, bool& fb)
 {
     constexpr int s = S;
     const int k = s * SH + v;
     const bool live = k < P;
     const int q = k + ((RC && k >= 4) ? 1 : 0);
     const int i = (q * 11) >> 5, j = q - 3 * i;          // q / 3 and q % 3 for q < 10
-    float px = fmaf(row_pick<SH, 2 * P>(offs, s * SH, v), x.scale, (float)(bx + j * x.dil));
-    float py = fmaf(row_pick<SH, 2 * P>(offs, P + s * SH, v), x.scale, (float)(by + i * x.dil));
-    float m = row_pick<SH, P>(msk, s * SH, v);
+    float px = fmaf(ox, x.scale, (float)(bx + j * x.dil));
+    float py = fmaf(oy, x.scale, (float)(by + i * x.dil));
     const bool valid = (px > -1.0f) & (px < x.fW) & (py > -1.0f) & (py < x.fH);
     bool ok = valid;
     if (!FULL) {
@@ -382,6 +412,28 @@ __device__ __forceinline__ SlotCoef slot_coef(const WinCtx& x, const RowLoad<DT,
     c.w11 = mly * lx;
     c.a00 = __mul24(y0, x.row16) + __mul24(x0, x.xstep) + ubase;
     return c;
+}
+
+// The slot's values picked from the unit's whole rows (the softmax variant,
+// whose weights need all of a unit's raw weights in every lane).
+template <int DT, int FULL, int RC, int P, int SH, int S, typename MR>
+__device__ __forceinline__ SlotCoef slot_coef(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
+                                              const MR& msk, int v, int bx, int by, int ubase,
+                                              bool& fb)
+{
+    return slot_coef_of<FULL, RC, P, SH, S>(x, row_pick<SH, 2 * P>(offs, S * SH, v),
+                                            row_pick<SH, 2 * P>(offs, P + S * SH, v),
+                                            row_pick<SH, P>(msk, S * SH, v), v, bx, by, ubase, fb);
+}
+
+// The slot's values from this lane's own loads.
+template <int DT, int FULL, int RC, int P, int SH, int S>
+__device__ __forceinline__ SlotCoef slot_coef(const WinCtx& x, const SlotRows<DT, P, SH>& sr, int v, int bx,
+                                              int by, int ubase, bool& fb)
+{
+    using E = Elem<DT>;
+    return slot_coef_of<FULL, RC, P, SH, S>(x, E::raw_to_f(sr.ox[S]), E::raw_to_f(sr.oy[S]),
+                                            E::raw_to_f(sr.m[S]), v, bx, by, ubase, fb);
 }
 
 // Lane v of every unit's lane group takes lane `src` of the same group.
@@ -494,6 +546,13 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
 
     RowLoad<DT, 2 * P> offs;
     RowLoad<DT, P> msk;
+    // shared coefficients over four lanes (raw weights): each lane loads its
+    // own points' values (stage-1 fp32: 66.5 -> 62.7 us, 116 -> 94 registers).
+    // Units of two lanes keep the row loads: bfloat16 element loads measured
+    // slower there (the 256x256 shape with sharing requested: 121.5 -> 128.8 us)
+    constexpr bool kSlotRows = SHARE == 4 && !SM;
+    SlotRows<DT, P, (SHARE ? SHARE : 1)> srows;
+    const int vshare = SHARE ? (int)(lane & (SHARE - 1)) : 0;
     // coalesced rows: with one group per workgroup and full-width tiles, unit
     // u of the tile is pixel oy0*Wo + u, so a wave's rows are evenly spaced
     const uint32_t off_row_bytes = (uint32_t)(a.off_row * s);
@@ -527,8 +586,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             unit_of(unit_of_item(threadIdx.x), oy, ox, gl);
             uint32_t so, sm;
             row_starts(min(oy, a.Ho - 1), min(ox, a.Wo - 1), gl, so, sm);
-            offs.issue(ro, so);
-            msk.issue(rm, sm);
+            if constexpr (kSlotRows) {
+                srows.issue(ro, rm, so, sm, vshare);
+            } else {
+                offs.issue(ro, so);
+                msk.issue(rm, sm);
+            }
         }
     };
 
@@ -635,7 +698,8 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         // SPLIT: this lane's vector of the unit
         const uint32_t vsub = SPLIT ? u - unit_of_item(u) * lpu : 0u;
         RowLoad<DT, 2 * P> co = offs;
-        if (!COAL) co.finish();
+        if (!COAL && !kSlotRows) co.finish();
+        const SlotRows<DT, P, (SHARE ? SHARE : 1)> csr = srows;
         if (COAL) {
             // this pass's rows, staged by the wave one pass ahead.  Issued
             // since then, in this order (the fences keep it): the staging
@@ -650,7 +714,7 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             wait_lds_reads();
         }
         RowLoad<DT, P> cm = msk;
-        cm.finish();
+        if (!kSlotRows) cm.finish();
         // the rows just read are unpacked here, before the next unit's rows
         // are requested into the same registers: a read of them sunk below
         // that request would keep both sets alive and force a copy of rows in
@@ -682,8 +746,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             int oy2, ox2, gl2;
             unit_of(unit_of_item(u + B), oy2, ox2, gl2);
             row_starts(min(oy2, a.Ho - 1), min(ox2, a.Wo - 1), gl2, nso, nsm);
-            offs.issue(ro, nso);
-            msk.issue(rm, nsm);
+            if constexpr (kSlotRows) {
+                srows.issue(ro, rm, nso, nsm, vshare);
+            } else {
+                offs.issue(ro, nso);
+                msk.issue(rm, nsm);
+            }
         }
         // (a whole-image window's units all lie inside the image)
         if (!FULL && (oy >= a.Ho || ox >= a.Wo)) return;
@@ -713,7 +781,10 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             SlotCoef sc[NS];
             static_for<NS>([&](auto sic) {
                 constexpr int si = decltype(sic)::value;
-                sc[si] = slot_coef<DT, FULL, RC, P, SHARE, si>(cx, co, mrow, v, bx, by, ucommon, fb);
+                if constexpr (kSlotRows)
+                    sc[si] = slot_coef<DT, FULL, RC, P, SHARE, si>(cx, csr, v, bx, by, ucommon, fb);
+                else
+                    sc[si] = slot_coef<DT, FULL, RC, P, SHARE, si>(cx, co, mrow, v, bx, by, ucommon, fb);
             });
             if (!FULL) {
                 // a unit is recomputed when any of its lanes found a point
