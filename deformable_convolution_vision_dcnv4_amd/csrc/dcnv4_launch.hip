@@ -15,7 +15,8 @@
 //       offsets (R = 5 unless tuned), for the smallest GB, when at most four
 //       bands (eight for units of three or more vectors) cover the image:
 //       band height chosen to minimise (rounds of workgroups) x (rows
-//       computed + rows staged / 2).  With more bands the margins cost more
+//       computed + rows staged / 2); a margin of R - 1 when that saves a
+//       whole round of workgroups.  With more bands the margins cost more
 //       staging than LDS saves, and large offsets (whose units fall back to
 //       global reads) make it worse;
 //     - else tiles of 16 x 64 outputs with a margin of 12 pixels (units of
@@ -157,29 +158,48 @@ bool plan_window(const Problem& p, Plan* pl)
         }
         if (GB) { full = 1; TH = p.Ho; TW = p.Wo; WH = p.H + 2; WW = p.W + 2; }
     }
-    // bands of full-width rows
-    for (int oi = 0; oi < no && !GB && t.full != 1; ++oi) {
-        const int gb = order[oi], slot = gb * ub;
-        const int ww = window_extent(t.tw ? t.tw : p.Wo, p.stride, p.K, p.dil, R, p.W);
+    // bands of full-width rows: the band height for margin r and groups gb
+    // that minimises (rounds of workgroups) x (rows computed + half the rows
+    // staged); false when no band fits or too many are needed
+    auto band_plan = [&](int gb, int r, int* th_out, int64_t* rounds_out) {
+        const int slot = gb * ub;
+        const int ww = window_extent(t.tw ? t.tw : p.Wo, p.stride, p.K, p.dil, r, p.W);
         int max_th = 0;
         for (int th = 1; th <= p.Ho; ++th) {
-            if (lds_for(window_extent(th, p.stride, p.K, p.dil, R, p.H), ww, slot) > kLdsPerCu) break;
+            if (lds_for(window_extent(th, p.stride, p.K, p.dil, r, p.H), ww, slot) > kLdsPerCu) break;
             max_th = th;
         }
         if (t.th) max_th = t.th;
-        if (max_th < 1) continue;
+        if (max_th < 1) return false;
         const int nb0 = (int)ceil_div(p.Ho, max_th);
-        if (nb0 > (lpu > 1 ? 8 : 4) && !t.th) continue;
-        // band count: fewest rounds of workgroups x (rows computed + half the rows staged)
+        if (nb0 > (lpu > 1 ? 8 : 4) && !t.th) return false;
         double best = 1e30;
         for (int nb = nb0; nb <= 2 * nb0; ++nb) {
             const int th = (int)ceil_div(p.Ho, nb);
             const int64_t wgs = (int64_t)p.N * ceil_div(p.Ho, th) * (p.G / gb);
             const int64_t rounds = ceil_div(wgs, cus);
-            const double cost = (double)rounds * (th + 0.5 * window_extent(th, p.stride, p.K, p.dil, R, p.H));
-            if (cost < best) { best = cost; TH = th; }
+            const double cost = (double)rounds * (th + 0.5 * window_extent(th, p.stride, p.K, p.dil, r, p.H));
+            if (cost < best) { best = cost; *th_out = th; *rounds_out = rounds; }
         }
-        GB = gb; TW = t.tw ? t.tw : p.Wo;
+        return true;
+    };
+    for (int oi = 0; oi < no && !GB && t.full != 1; ++oi) {
+        int th = 0;
+        int64_t rounds = 0;
+        if (!band_plan(order[oi], R, &th, &rounds)) continue;
+        // one pixel less of margin when that saves a whole round of
+        // workgroups (stage-1 fp32: two bands of 28 rows with margin 4,
+        // 60.3 us, against three of 19 with margin 5, 62.6 us).  A smaller
+        // margin sends more points to the global fallback, so it is not
+        // taken otherwise (the latent shape with margin 4: 54.6 against
+        // 52.5 us at the same band count)
+        int th4 = 0;
+        int64_t rounds4 = 0;
+        if (t.r < 0 && R > 1 && band_plan(order[oi], R - 1, &th4, &rounds4) && rounds4 < rounds) {
+            th = th4;
+            R = R - 1;
+        }
+        GB = order[oi]; TH = th; TW = t.tw ? t.tw : p.Wo;
     }
     // tiles of 16 x 64 outputs with a 12-pixel margin, one lane per vector,
     // when rows are too wide for bands (the 256x256 shape: 126 against 179 us

@@ -124,7 +124,7 @@ def test_plan_kernel_family_and_read_width(dtype, Cg, xoff, K, kernel, vec):
 @pytest.mark.parametrize("N,dtype,kernel,tile_h,grid", [
     (1, 1, "direct", 0, 98), (4, 1, "direct", 0, 392), (8, 1, "window", 7, 256),
     (16, 1, "window", 14, 256), (32, 1, "window", 28, 256), (64, 1, "window", 56, 256),
-    (8, 0, "window", 7, 256), (64, 0, "window", 19, 768)])
+    (8, 0, "window", 7, 256), (64, 0, "window", 28, 512)])
 def test_plan_fills_the_gpu_at_small_batches(N, dtype, kernel, tile_h, grid):
     """Stage-1 shape (56x56, 4 groups of 16): a whole-image window per
     (image, group) leaves CUs idle below 64 images, so the plan takes more
@@ -136,6 +136,16 @@ def test_plan_fills_the_gpu_at_small_batches(N, dtype, kernel, tile_h, grid):
     assert d["kernel"] == kernel and pl.grid == grid
     if kernel == "window":
         assert pl.tile_h == tile_h and pl.tile_w == 56
+
+
+def test_band_margin_drops_by_one_only_to_save_a_round():
+    """Bands with a margin of 5 rows; 4 when that saves a whole round of
+    workgroups (stage-1 fp32 at batch 64: two bands of 28 rows instead of
+    three of 19), not when the round count is the same (the latent shape)."""
+    st, pl = plan(dtype=0, Cg=16, N=64, H=56, W=56, G=4)
+    assert st == OK and (pl.tile_h, pl.margin_y, pl.grid) == (28, 4, 512)
+    st, pl = plan(dtype=2, Cg=40, N=8, H=64, W=64, G=8)
+    assert st == OK and (pl.tile_h, pl.margin_y, pl.grid) == (8, 5, 512)
 
 
 def test_plan_tuning_variable_is_read_again_when_it_changes(monkeypatch):
