@@ -28,7 +28,8 @@ bytes per launch measured by rocprofv3 counters on the same kernel source
 = the L2 hit rate from the same counter runs (TCC_HIT / (TCC_HIT + TCC_MISS)).
 `configs` = every other measured configuration (the five workloads' I/O
 types), event-timed in the same run the same way, with each one's fraction
-of sampling points outside the image; then the backward, the DCNv3-style
+of sampling points outside the image, and the stage-1 shape with spatially
+smooth offsets (a sensitivity input, marked as such); then the backward, the DCNv3-style
 variant and the module forward on the named workload (algorithmic bytes:
 the backward's inputs read and binary32 gradients written; the module's
 input read, output written and weights).  `cpu_baseline` = the CPU oracle on
@@ -155,13 +156,13 @@ def main():
 
     from deformable_convolution_vision_dcnv4_amd import binding
     from deformable_convolution_vision_dcnv4_amd import inputs as gen
-    from deformable_convolution_vision_dcnv4_amd.workloads import CONFIGS, WORKLOADS, oob_fractions
+    from deformable_convolution_vision_dcnv4_amd.workloads import CONFIGS, SENSITIVITY, WORKLOADS, oob_fractions
 
     def log(*a):
         if not args.quiet:
             print("[bench]", *a, file=sys.stderr, flush=True)
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[args.workload] if args.workload in WORKLOADS else SENSITIVITY[args.workload]
     if args.batch is not None and args.batch != wl.N:
         if args.batch < 1:
             ap.error("--batch must be at least 1")
@@ -307,10 +308,12 @@ def main():
     # the other configurations, timed the same way (launch-to-launch events)
     configs = []
     if args.op == "forward" and not args.no_configs and args.batch is None:
-        for name, cdt in CONFIGS:
+        # then the sensitivity inputs (smooth offsets), marked as such
+        sens = [(n, d) for n, swl in SENSITIVITY.items() for d in swl.dtypes]
+        for name, cdt in list(CONFIGS) + sens:
             if (name, cdt) == (wl.name, dtype):
                 continue
-            cwl = WORKLOADS[name]
+            cwl = WORKLOADS[name] if name in WORKLOADS else SENSITIVITY[name]
             cr = measure(cwl, cdt, "forward", args.config_steps, max(5, args.warmup // 4), args.rotate_bytes,
                          per_launch=False, spinup_s=min(args.spinup_s, 0.3))
             cbytes = cwl.algorithmic_bytes(cdt)
@@ -329,6 +332,10 @@ def main():
                 "l2_hit": ccnt.get("l2_hit") if ccnt else None,
                 "hbm_traffic": ccnt.get("hbm_bytes_per_launch") if ccnt else None,
             })
+            if name in SENSITIVITY:
+                configs[-1]["sensitivity"] = (f"offsets box-filtered over {2 * cwl.offset_smooth + 1}x"
+                                              f"{2 * cwl.offset_smooth + 1} output pixels, same standard "
+                                              "deviation; reported beside the workloads, not instead of them")
         # the other operations on this workload: backward, the DCNv3-style
         # variant and the whole module forward, event-timed the same way
         from deformable_convolution_vision_dcnv4_amd.workloads import module_bytes
@@ -376,7 +383,7 @@ def main():
             "N": wl.N, "H": wl.H, "W": wl.W, "G": wl.G, "Cg": wl.Cg, "K": wl.K,
             "stride": wl.stride, "pad": wl.pad, "dilation": wl.dil, "offset_scale": wl.offset_scale,
             "inputs": {"x": list(wl.x_dist), "offset": list(wl.offset_dist), "mask": list(wl.mask_dist),
-                       "seed": wl.seed},
+                       "seed": wl.seed, "offset_smooth_radius": wl.offset_smooth},
             "algorithmic_bytes_per_step": alg_bytes,
             "samples_per_step": wl.samples(),
             "rotating_copies": r["copies"],

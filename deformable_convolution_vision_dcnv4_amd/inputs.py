@@ -14,6 +14,11 @@ Generator (counter-based, so any element can be produced independently):
   normal(i)  = sqrt(-2 ln(1 - u(2i))) * cos(2 pi u(2i+1))   (Box-Muller, float64)
 Values are scaled in float64, rounded to float32 (nearest even), then to the
 I/O type (nearest even).  Streams: x = 0, offset = 1, mask = 2.
+Smooth offsets (a workload's offset_smooth = r > 0): the float64 offset draws,
+as [N, Ho, Wo, channel], are summed over the (2r+1) x (2r+1) output pixels
+around each pixel (the image wrapping around at its edges) and divided by
+2r+1, so each offset is still normal with the same standard deviation while
+neighbours share most of their terms; then rounded as above.
 """
 import numpy as np
 
@@ -64,6 +69,18 @@ def draw(seed, stream, count, dist):
     return out
 
 
+def box_smooth(a, r):
+    """Sum of a [N, H, W, C] float64 array over the (2r+1)^2 pixels around
+    each pixel (wrapping around), divided by 2r+1."""
+    rows = np.zeros_like(a)
+    for dy in range(-r, r + 1):
+        rows += np.roll(a, dy, axis=1)
+    out = np.zeros_like(a)
+    for dx in range(-r, r + 1):
+        out += np.roll(rows, dx, axis=2)
+    return out / (2 * r + 1)
+
+
 def to_io(values_f64, dtype):
     """float64 -> float32 (RNE) -> I/O type (RNE).  bf16 comes back as uint16 bits."""
     f32 = np.asarray(values_f64, dtype=np.float64).astype(np.float32)
@@ -85,6 +102,9 @@ def make_inputs(wl, dtype, seed=None, integer_offsets=False):
     npix = wl.N * Ho * Wo
     x = draw(seed, STREAM_X, nx, wl.x_dist)
     off = draw(seed, STREAM_OFFSET, npix * wl.G * 2 * wl.P, wl.offset_dist)
+    r = getattr(wl, "offset_smooth", 0)
+    if r > 0:
+        off = box_smooth(off.reshape(wl.N, Ho, Wo, wl.G * 2 * wl.P), r).reshape(-1)
     if integer_offsets:
         off = np.rint(off)
     m = draw(seed, STREAM_MASK, npix * wl.G * wl.P, wl.mask_dist)

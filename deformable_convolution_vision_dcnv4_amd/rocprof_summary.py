@@ -31,7 +31,7 @@ import statistics
 import sys
 
 from . import build
-from .workloads import WORKLOADS, module_bytes
+from .workloads import SENSITIVITY, WORKLOADS, module_bytes
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 OP_KERNEL_PREFIXES = ("void dcnv4::", "dcnv4::")
@@ -130,7 +130,7 @@ def main(argv=None):
                     help="the command line of the counter runs (COUNTER = FETCH_SIZE, then WRITE_SIZE)")
     ap.add_argument("--out", required=True, help="output path prefix")
     a = ap.parse_args(argv)
-    wl = WORKLOADS[a.workload]
+    wl = WORKLOADS[a.workload] if a.workload in WORKLOADS else SENSITIVITY[a.workload]
     s = {"f32": 4, "f16": 2, "bf16": 2}[a.dtype]
     Ho, Wo = wl.out_hw()
     x_b = wl.N * wl.H * wl.W * wl.C * s

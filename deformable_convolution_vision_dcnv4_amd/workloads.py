@@ -34,6 +34,8 @@ class Workload:
     offset_scale: float = 1.0
     remove_center: bool = False
     seed: int = 0
+    # offsets low-pass filtered over (2r+1) x (2r+1) output pixels (0: i.i.d.)
+    offset_smooth: int = 0
     note: str = field(default="", compare=False)
 
     @property
@@ -96,6 +98,20 @@ WORKLOADS = {
                           offset_dist=("normal", 2.0),
                           mask_dist=("normal", 1.0 / math.sqrt(8.0)),
                           note="diffusion U-Net latent shape, Cg=40"),
+}
+
+
+# Sensitivity input, reported beside the workloads, never instead of them:
+# trained offsets come from a depthwise 3x3 and a linear projection of
+# spatially correlated features, so neighbouring pixels' offsets are alike,
+# where the workloads' i.i.d. offsets are the harsher case.  Same shape,
+# distributions and seed as fiit_stage1; offsets box-filtered over 5 x 5
+# output pixels and rescaled to the same standard deviation.
+SENSITIVITY = {
+    "fiit_stage1_smooth": Workload("fiit_stage1_smooth", 64, 56, 56, 4, 16, ("f16",),
+                                   offset_dist=("normal", 1.5), mask_dist=("normal", 0.5),
+                                   offset_smooth=2,
+                                   note="stage-1 shape, spatially smooth offsets (sensitivity)"),
 }
 
 

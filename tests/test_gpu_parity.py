@@ -14,7 +14,7 @@ import torch
 
 from deformable_convolution_vision_dcnv4_amd import binding
 from deformable_convolution_vision_dcnv4_amd import inputs as gen
-from deformable_convolution_vision_dcnv4_amd.workloads import WORKLOADS, Workload
+from deformable_convolution_vision_dcnv4_amd.workloads import SENSITIVITY, WORKLOADS, Workload
 from oracle import ref
 from tests import gpu_util as gu
 from tests import helpers as H
@@ -71,6 +71,19 @@ def test_workload_parity_full_size(name, dtype):
     got = run_gpu(x, off, m, dtype, **kw_of(wl))
     _, _, mism = gu.compare(got, want, dtype, label=name)
     assert mism == 0, f"{mism} outputs differ in bits from the oracle's binary32 sequence"
+
+
+@pytest.mark.parametrize("name", list(SENSITIVITY))
+def test_sensitivity_inputs_full_size(name):
+    """The smooth-offset sensitivity input at full size, as the bench times it."""
+    wl = SENSITIVITY[name]
+    for dtype in wl.dtypes:
+        gu.announce(f"sensitivity {wl.describe(dtype)} smooth {wl.offset_smooth} seed {wl.seed}")
+        x, off, m = gen.make_inputs(wl, dtype)
+        want = ref.forward_f32(x, off, m, dtype=dtype, **okw_of(wl))
+        got = run_gpu(x, off, m, dtype, **kw_of(wl))
+        _, _, mism = gu.compare(got, want, dtype, label=name)
+        assert mism == 0, f"{mism} outputs differ in bits from the oracle's binary32 sequence"
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from deformable_convolution_vision_dcnv4_amd import inputs as gen
-from deformable_convolution_vision_dcnv4_amd.workloads import WORKLOADS
+from deformable_convolution_vision_dcnv4_amd.workloads import SENSITIVITY, WORKLOADS
 
 
 def test_splitmix_known_values():
@@ -69,3 +69,27 @@ def test_workload_byte_counts():
     assert WORKLOADS["hires"].algorithmic_bytes("bf16") == 123731968
     assert WORKLOADS["sd_latent"].algorithmic_bytes("bf16") == 56098816
     assert WORKLOADS["sd_latent"].mask_dist[1] == pytest.approx(1 / math.sqrt(8))
+
+
+def test_smooth_offsets_keep_the_distribution_and_correlate_neighbours():
+    """Box-filtered offsets (radius 2, divided by 5): still N(0, sigma) per
+    element, while horizontally adjacent pixels share 20 of their 25 terms
+    (correlation 4/5); the other tensors and the offsets' draws are those
+    of the unsmoothed workload."""
+    import dataclasses
+    wl = dataclasses.replace(SENSITIVITY["fiit_stage1_smooth"], N=4)
+    base = dataclasses.replace(wl, offset_smooth=0)
+    x, off, m = gen.make_inputs(wl, "f32")
+    x0, off0, m0 = gen.make_inputs(base, "f32")
+    assert np.array_equal(x, x0) and np.array_equal(m, m0)
+    o = off.astype(np.float64)
+    assert abs(o.std() / 1.5 - 1.0) < 0.02 and abs(o.mean()) < 0.02
+    a, b = o[:, :, :-1, :].ravel(), o[:, :, 1:, :].ravel()
+    assert abs(np.corrcoef(a, b)[0, 1] - 0.8) < 0.02
+    # the box sum written out for one element, against the vectorised form
+    raw = gen.draw(wl.seed, gen.STREAM_OFFSET, off0.size, wl.offset_dist).reshape(off0.shape)
+    n, y, xx, c = 1, 0, 55, 7
+    s = sum(raw[n, (y + dy) % 56, (xx + dx) % 56, c] for dy in range(-2, 3) for dx in range(-2, 3)) / 5
+    assert np.float32(s) == off[n, y, xx, c]
+    # radius 0 is the identity
+    assert np.array_equal(gen.box_smooth(raw, 0), raw)
