@@ -119,3 +119,19 @@ def test_source_hash_is_stable_and_short():
     assert h == build.source_hash() and len(h) == 16
     f = build.source_hash("forward")
     assert f == build.source_hash("forward") and len(f) == 16 and f != h
+
+
+def test_committed_counter_records_match_the_forward_source():
+    """Every measured configuration has a counter record in profiles/ taken on
+    the current forward kernel source (bench.py reports the record's HBM
+    traffic and L2 hit rate only when the source hashes agree)."""
+    from deformable_convolution_vision_dcnv4_amd.workloads import CONFIGS
+    root = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+    want = build.source_hash("forward")
+    for name, dtype in CONFIGS:
+        path = os.path.join(root, f"{name}_{dtype}_hbm_counters.json")
+        assert os.path.exists(path), path
+        with open(path) as fh:
+            rec = json.load(fh)
+        assert rec["kernel_source_hash"] == want, f"{path} was taken on another forward source"
+        assert rec["hbm_bytes_per_launch"] > 0 and 0.0 < rec["l2_hit"] < 1.0
