@@ -192,7 +192,7 @@ struct WinCtx {
 template <int DT, int NV, int FULL, int RC, int P, int SPLIT, typename MR>
 __device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowLoad<DT, 2 * P>& offs,
                                                      const MR& msk, int k, int bx, int by,
-                                                     const char* ub, bool& fb)
+                                                     int ubase, bool& fb)
 {
     PointRegs<NV> r;
     const int q = (RC && k >= 4) ? k + 1 : k;
@@ -222,9 +222,12 @@ __device__ __forceinline__ PointRegs<NV> issue_point(const WinCtx& x, const RowL
     r.w01 = mhy * lx;
     r.w10 = mly * hx;
     r.w11 = mly * lx;
-    // ub: the unit's vector 0 at window pixel (0, 0) of this LDS (its base
-    // added once per unit, not once per point)
-    const char* p00 = ub + (__mul24(y0, x.row16) + (SPLIT ? __mul24(x0, x.xstep) : (x0 << 4)));
+    // ubase: the LDS byte of image pixel (0, 0) for the unit's vector 0 (it
+    // may lie before the window, so it is added to the point's offset as an
+    // integer: the corner's byte a00 is never negative, and every pointer
+    // formed here stays inside the LDS allocation)
+    const int a00 = __mul24(y0, x.row16) + (SPLIT ? __mul24(x0, x.xstep) : (x0 << 4)) + ubase;
+    const char* p00 = x.lbase + a00;
     const char* p10 = p00 + x.row16;
     const int step01 = SPLIT ? x.xstep : 16;
 #pragma unroll
@@ -808,12 +811,11 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
             });
         } else {
             // two points in flight: issue the reads of point k+1, then accumulate point k
-            const char* ub = cx.lbase + ubase;
-            PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, 0, bx, by, ub, fb);
+            PointRegs<NV> cur = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, 0, bx, by, ubase, fb);
 #pragma unroll
             for (int k = 0; k < P; ++k) {
                 PointRegs<NV> nxt;
-                if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, k + 1, bx, by, ub, fb);
+                if (k + 1 < P) nxt = issue_point<DT, NV, FULL, RC, P, SPLIT>(cx, co, mrow, k + 1, bx, by, ubase, fb);
                 fence_sched();
                 pin(cur);
                 consume_point<DT, NV>(acc, cur);
