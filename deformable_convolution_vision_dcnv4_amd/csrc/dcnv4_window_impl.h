@@ -555,6 +555,12 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
     // slower there (the 256x256 shape with sharing requested: 121.5 -> 128.8 us)
     constexpr bool kSlotRows = SHARE == 4 && !SM;
     SlotRows<DT, P, (SHARE ? SHARE : 1)> srows;
+    if constexpr (kSlotRows) {
+        // the row loads are not used on this path: defined values for the
+        // copies below, which the compiler then drops
+        offs = RowLoad<DT, 2 * P>{};
+        msk = RowLoad<DT, P>{};
+    }
     const int vshare = SHARE ? (int)(lane & (SHARE - 1)) : 0;
     // coalesced rows: with one group per workgroup and full-width tiles, unit
     // u of the tile is pixel oy0*Wo + u, so a wave's rows are evenly spaced
@@ -702,7 +708,8 @@ k_window(KArgs a, uint32_t total_blocks, uint32_t per_xcd)
         const uint32_t vsub = SPLIT ? u - unit_of_item(u) * lpu : 0u;
         RowLoad<DT, 2 * P> co = offs;
         if (!COAL && !kSlotRows) co.finish();
-        const SlotRows<DT, P, (SHARE ? SHARE : 1)> csr = srows;
+        SlotRows<DT, P, (SHARE ? SHARE : 1)> csr;
+        if constexpr (kSlotRows) csr = srows;
         if (COAL) {
             // this pass's rows, staged by the wave one pass ahead.  Issued
             // since then, in this order (the fences keep it): the staging
