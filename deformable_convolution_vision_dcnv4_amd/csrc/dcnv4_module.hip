@@ -766,18 +766,13 @@ __global__ void __launch_bounds__(256) k_dw3x3v(const void* __restrict__ xn, voi
         hy = (int)(row - img * H);
     }
     const int c0 = ch * VE, wx0 = run * PX;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(static_cast<const char*>(xn) + img * H * W * C * s, (uint32_t)((int64_t)H * W * C * s));
-    // v[ii][j]: row hy + ii - 1, column wx0 + j - 1
-    u32x4 v[3][PX + 2];
-#pragma unroll
-    for (int ii = 0; ii < 3; ++ii)
-#pragma unroll
-        for (int j = 0; j < PX + 2; ++j) {
-            const int y = hy + ii - 1, xx = wx0 + j - 1;
-            const bool in = (y >= 0) & (y < H) & (xx >= 0) & (xx < W);
-            v[ii][j] = buf_load16(r, in ? (uint32_t)((((int64_t)y * W + xx) * C + c0) * s) : kOobOffset);
-        }
+    // one resource over the whole tensor (the host launches this kernel only
+    // when it is under 2 GiB, so 32-bit offsets fit and stay below the
+    // out-of-range offset): the same for every lane, where one per image
+    // would make the compiler loop over the lanes' distinct resources at
+    // every load
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(xn, (uint32_t)((int64_t)N * H * W * C * s));
+    const uint32_t pstep = (uint32_t)C * s;                  // bytes per pixel
     float acc[PX][VE];
 #pragma unroll
     for (int q = 0; q < VE / 4; ++q) {
@@ -787,23 +782,46 @@ __global__ void __launch_bounds__(256) k_dw3x3v(const void* __restrict__ xn, voi
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[px][4 * q + e] = b4[e];
     }
+    // one input row at a time: its PX + 2 vectors, then its three taps on the
+    // PX outputs.  (With all three rows loaded up front the compiler widened
+    // all 18 vectors at once, about 190 registers and two waves per SIMD.)
 #pragma unroll
-    for (int k = 0; k < 9; ++k) {
-        const int ii = k / 3, jj = k % 3;
-        float tk[VE];
+    for (int ii = 0; ii < 3; ++ii) {
+        const int y = hy + ii - 1;
+        const uint32_t o0 = (((uint32_t)img * (uint32_t)H + (uint32_t)y) * (uint32_t)W + (uint32_t)(wx0 - 1)) * pstep +
+                            (uint32_t)c0 * s;
+        u32x4 v[PX + 2];
 #pragma unroll
-        for (int q = 0; q < VE / 4; ++q) {
-            const f4 t4 = *reinterpret_cast<const f4*>(&wl[k * C + c0 + 4 * q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tk[4 * q + e] = t4[e];
+        for (int j = 0; j < PX + 2; ++j) {
+            const int xx = wx0 + j - 1;
+            const bool in = (y >= 0) & (y < H) & (xx >= 0) & (xx < W);
+            v[j] = buf_load16(r, in ? o0 + (uint32_t)j * pstep : kOobOffset);
         }
 #pragma unroll
-        for (int px = 0; px < PX; ++px) {
-            float f[VE];
-            load_vals<DT, VE>(&v[ii][px + jj], f);
+        for (int jj = 0; jj < 3; ++jj) {
+            const int k = ii * 3 + jj;
+            float tk[VE];
 #pragma unroll
-            for (int e = 0; e < VE; ++e) acc[px][e] = fmaf(tk[e], f[e], acc[px][e]);
+            for (int q = 0; q < VE / 4; ++q) {
+                const f4 t4 = *reinterpret_cast<const f4*>(&wl[k * C + c0 + 4 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tk[4 * q + e] = t4[e];
+            }
+#pragma unroll
+            for (int px = 0; px < PX; ++px) {
+                float f[VE];
+                load_vals<DT, VE>(&v[px + jj], f);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc[px][e] = fmaf(tk[e], f[e], acc[px][e]);
+            }
         }
+        // the next row's loads are issued after this row's multiply-adds (the
+        // accumulators are pinned here, and the loads cannot cross the fence)
+#pragma unroll
+        for (int px = 0; px < PX; ++px)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) asm volatile("" : "+v"(acc[px][e]));
+        asm volatile("" ::: "memory");
     }
     char* o = static_cast<char*>(d) + ((img * H + hy) * (int64_t)W * C + c0) * s;
 #pragma unroll
@@ -967,9 +985,11 @@ hipError_t run(const ModuleProblem& m, hipStream_t st)
         // taps through LDS when they fit in 64 KiB (up to 1638 channels)
         const size_t wbytes = (size_t)C * 10 * sizeof(float);
         const bool lw = wbytes <= 64 * 1024;
+        // the vector kernel addresses the whole tensor with 31-bit offsets
+        const bool small = (int64_t)npix * C * (int64_t)sizeof(typename Elem<DT>::S) < ((int64_t)1 << 31);
         const unsigned grid = (unsigned)cdiv(npix * (vec ? C / VE : C), 256);
         constexpr int PX = 4;
-        if (vec && lw)
+        if (vec && lw && small)
             hipLaunchKernelGGL((k_dw3x3v<DT, PX>), dim3((unsigned)cdiv((int64_t)m.N * m.H * cdiv(m.W, PX) * (C / VE),
                                                                        256)),
                                dim3(256), wbytes, st, xn, d, m.w.w_dw, m.w.b_dw, m.N, m.H, m.W, C);
